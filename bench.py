@@ -1,0 +1,242 @@
+"""Benchmark of the MXFP4 attention hot path on one MI355X.
+
+A step is one pass of the forward hot path over one batch: MXFP4 quantization of Q, K (along d)
+and V (along the sequence, transposed) followed by the fused FP4 attention forward, on the
+video-DiT-shaped workload B=1, H=24, N=32768, d=128, non-causal.  Inputs (bf16) are resident in
+HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
+
+Printed: one JSON line with the step throughput, a roofline object for the dominant kernel (the
+fused forward, timed alone with HIP events on the stream it runs on), the backward of the QAT
+workload (B=1, H=16, N=8192, d=128) measured the same way, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 attn fwd TFLOPS (4·B·H·N²·d) at N=32K,d=128; % of MXFP4 MFMA peak"
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak (published 10.1 PFLOP/s)
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published 8 TB/s)
+QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gen_inputs(w, tensors):
+    """Seeded synthetic inputs of the workload, generated per head in parallel processes."""
+    import numpy as np
+    from concurrent.futures import ProcessPoolExecutor
+    from bit_attention_amd import workloads as W
+    out = {}
+    with ProcessPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        for t in tensors:
+            H = W.heads_of(w, t)
+            jobs = [(b, h) for b in range(w.B) for h in range(H)]
+            heads = list(ex.map(_gen_one, [(w.name, t, b, h) for b, h in jobs]))
+            arr = np.empty((w.B, H, w.N, w.d), dtype=np.float32)
+            for (b, h), x in zip(jobs, heads):
+                arr[b, h] = x
+            out[t] = arr
+    return out
+
+
+def _gen_one(a):
+    from bit_attention_amd import workloads as W
+    name, t, b, h = a
+    return W.gen_head(W.WORKLOADS[name], t, b, h)
+
+
+def time_region(fn, reps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(w, seconds_target=15.0):
+    """The oracle, untouched, on a bounded sample of the same workload (one head, sampled rows)."""
+    import numpy as np
+    import oracle
+    from bit_attention_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    q = W.gen_head(w, "q", 0, 0)[None, None]
+    k = W.gen_head(w, "k", 0, 0)[None, None]
+    v = W.gen_head(w, "v", 0, 0)[None, None]
+    rows = W.sample_rows(w.N, 32)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    # grow the sample toward ~seconds_target of CPU work
+    n = int(min(w.N, max(32, 32 * seconds_target / max(dt, 1e-3))))
+    rows = W.sample_rows(w.N, n)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows.size * w.N * w.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "sample": "float64 NumPy oracle forward (quantize K,V of head (0,0), then %d sampled query rows "
+                      "against all %d keys) in %.1f s; metric flops 4*rows*N*d" % (rows.size, w.N, dt),
+            "seconds": dt}
+
+
+def bench_backward(args, torch, ops, W):
+    w = W.WORKLOADS["qat_bwd_b1h16n8192d128"]
+    x = gen_inputs(w, ["q", "k", "v", "do"])
+    dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
+    qc, qs = ops.attn_fp4_quantize(dev["q"], 0)
+    kc, ks = ops.attn_fp4_quantize(dev["k"], 0)
+    vc, vs = ops.attn_fp4_quantize(dev["v"], 1)
+    o, m, l = ops.attn_fp4_fwd(qc, qs, kc, ks, vc, vs)
+    try:
+        res = ops.attn_fp4_bwd_recompute(qc, qs, kc, ks, vc, vs, o, dev["do"], m, l)
+    except ops.AttnFp4Error as e:
+        return {"workload": w.name, "status": str(e)}
+    dq, dk, dv = res
+    ws = torch.empty(ops.attn_fp4_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: ops.attn_fp4_bwd_recompute(qc, qs, kc, ks, vc, vs, o, dev["do"], m, l, dq=dq, dk=dk, dv=dv,
+                                            workspace=ws)
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    ms = time_region(fn, max(3, args.steps), stream)
+    pairs = w.B * w.Hq * w.N * w.N
+    fp4 = 2.0 * w.d * pairs
+    bf16 = 8.0 * w.d * pairs
+    t_roof = fp4 / (PEAK_FP4_TFLOPS * 1e9) + bf16 / (PEAK_BF16_TFLOPS * 1e9)
+    return {"workload": w.name, "ms": ms, "fp4_flops": fp4, "bf16_flops": bf16,
+            "tflops_total": (fp4 + bf16) / ms / 1e9, "roofline_ms": t_roof, "frac": t_roof / ms}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--fwd-only-reps", type=int, default=0,
+                    help="if > 0: only run the forward kernel this many times (for profilers)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the single-GPU kernel is what scales; see the sharding notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_attention_amd import ops
+    from bit_attention_amd import workloads as W
+
+    w = W.WORKLOADS["dit_b1h24n32768d128"]
+    log("generating inputs for", w.name)
+    t0 = time.perf_counter()
+    x = gen_inputs(w, ["q", "k", "v"])
+    log("  %.1f s" % (time.perf_counter() - t0))
+    dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
+    del x
+    B, H, N, d = w.B, w.Hq, w.N, w.d
+    qc = torch.empty((B, H, N, d // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device="cuda")
+    kc, ks = torch.empty_like(qc), torch.empty_like(qs)
+    vc = torch.empty((B, H, d, N // 2), dtype=torch.uint8, device="cuda")
+    vs = torch.empty((B, H, d, N // 32), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    m = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    l = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def quantize():
+        ops.attn_fp4_quantize(dev["q"], 0, qc, qs)
+        ops.attn_fp4_quantize(dev["k"], 0, kc, ks)
+        ops.attn_fp4_quantize(dev["v"], 1, vc, vs)
+
+    def fwd():
+        ops.attn_fp4_fwd(qc, qs, kc, ks, vc, vs, causal=w.causal, o=o, m=m, l=l)
+
+    def step():
+        quantize()
+        fwd()
+
+    if args.fwd_only_reps > 0:
+        quantize()
+        for _ in range(args.fwd_only_reps):
+            fwd()
+        torch.cuda.synchronize()
+        log("ran the forward %d times" % args.fwd_only_reps)
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    # timed region: exactly K steps, synchronised on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = time_region(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log("step %.3f ms (events), %.3f ms (wall)" % (ms_step, wall_ms))
+    # dominant kernel alone (same launch configuration), HIP events on its stream
+    fwd_ms = time_region(fwd, args.steps, stream)
+    quant_ms = time_region(quantize, args.steps, stream)
+    flops = 4.0 * B * H * N * N * d
+    fwd_tflops = flops / fwd_ms / 1e9
+    log("fwd kernel %.3f ms = %.1f TFLOPS; quantize q,k,v %.3f ms" % (fwd_ms, fwd_tflops, quant_ms))
+
+    result = {
+        "metric": METRIC,
+        "value": flops / ms_step / 1e9,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "step": "quantize Q,K,V (bf16->MXFP4) + fused FP4 attention forward",
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / PEAK_FP4_TFLOPS, "traffic": None,
+                     "kernel": "attn_fp4 forward (fwd_kernel<128,...,false>)", "kernel_ms": fwd_ms,
+                     "flops_per_launch": flops},
+        "quantize": {"ms": quant_ms, "elements": 3 * B * H * N * d,
+                     "gbps": QUANT_BYTES_PER_ELEM * 3 * B * H * N * d / quant_ms / 1e6,
+                     "frac_hbm": QUANT_BYTES_PER_ELEM * 3 * B * H * N * d / quant_ms / 1e6 / PEAK_HBM_GBS},
+    }
+    if not args.no_backward:
+        result["backward"] = bench_backward(args, torch, ops, W)
+        log("backward", result["backward"])
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cb = cpu_baseline(w)
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+// C-ABI host layer of libattnfp4: argument validation, device check, launch.
+// No allocation, no synchronisation, no printing; every error is a status code.
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/attn_fp4.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of the "is gfx950" check: 0 unknown, 1 yes, 2 no.
+int g_arch_ok[64];
+
+int32_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_FP4_E_HIP;
+  if (dev < 0) return ATTN_FP4_E_HIP;
+  if (dev < 64 && g_arch_ok[dev] == 1) return ATTN_FP4_OK;
+  if (dev < 64 && g_arch_ok[dev] == 2) return ATTN_FP4_E_UNSUPPORTED_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_FP4_E_HIP;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev] = ok ? 1 : 2;
+  return ok ? ATTN_FP4_OK : ATTN_FP4_E_UNSUPPORTED_DEVICE;
+}
+
+float resolve_scale(float s, int64_t d) { return s > 0.0f ? s : (float)(1.0 / std::sqrt((double)d)); }
+
+int32_t check_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return ATTN_FP4_E_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_FP4_E_INVALID_ARG;
+  if (N % 64 != 0 || Hq % Hkv != 0) return ATTN_FP4_E_INVALID_ARG;
+  // grid sizes: (N / 64) * Hq * B workgroups must fit a 32-bit grid dimension
+  if ((N / 64) * Hq * B > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  return ATTN_FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_fp4_abi_version(void) { return kAbiVersion; }
+
+const char* attn_fp4_status_string(int32_t status) {
+  switch (status) {
+    case ATTN_FP4_OK: return "ok";
+    case ATTN_FP4_E_INVALID_ARG: return "invalid argument (pointer, alignment, shape or enum)";
+    case ATTN_FP4_E_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 / MI355X required)";
+    case ATTN_FP4_E_UNSUPPORTED: return "unsupported configuration in this build";
+    case ATTN_FP4_E_HIP: return "HIP runtime or kernel launch error";
+    case ATTN_FP4_E_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int32_t attn_fp4_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32_t axis, void* codes,
+                          void* scales, void* stream) {
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return ATTN_FP4_E_INVALID_ARG;
+  if (bh <= 0 || n <= 0 || d <= 0) return ATTN_FP4_E_INVALID_ARG;
+  if (axis != 0 && axis != 1) return ATTN_FP4_E_INVALID_ARG;
+  if (d % 32 != 0) return ATTN_FP4_E_INVALID_ARG;
+  if (axis == 1 && (n % 32 != 0 || bh > 65535 || (n + 127) / 128 > 0x7FFFFFFF)) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  hipError_t e = attnfp4::launch_quantize(x, bh, n, d, axis, codes, scales, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_dims(a->B, a->Hq, a->Hkv, a->N, a->d);
+  if (st != ATTN_FP4_OK) return st;
+  const void* ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes,
+                        a->v_scales, a->o, a->m, a->l};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
+  if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  attnfp4::FwdParams p;
+  p.q_codes = (const uint8_t*)a->q_codes;
+  p.q_scales = (const uint8_t*)a->q_scales;
+  p.k_codes = (const uint8_t*)a->k_codes;
+  p.k_scales = (const uint8_t*)a->k_scales;
+  p.v_codes = (const uint8_t*)a->v_codes;
+  p.v_scales = (const uint8_t*)a->v_scales;
+  p.o = (uint16_t*)a->o;
+  p.m = a->m;
+  p.l = a->l;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.N = a->N;
+  const double s = resolve_scale(a->softmax_scale, a->d);
+  p.c = (float)(s * 1.4426950408889634);
+  p.scale_nat = (float)s;
+  hipError_t e = attnfp4::launch_fwd(p, (int)a->d, a->causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+  if (check_dims(B, Hq, Hkv, N, d) != ATTN_FP4_OK) return -1;
+  return attnfp4::bwd_workspace_bytes(B, Hq, N, d);
+}
+
+int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_dims(a->B, a->Hq, a->Hkv, a->N, a->d);
+  if (st != ATTN_FP4_OK) return st;
+  const void* ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes, a->v_scales,
+                        a->o, a->do_, a->m, a->l, a->dq, a->dk, a->dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
+  if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
+  const int64_t need = attnfp4::bwd_workspace_bytes(a->B, a->Hq, a->N, a->d);
+  if (a->workspace == nullptr || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 ||
+      a->workspace_bytes < need)
+    return ATTN_FP4_E_WORKSPACE;
+  st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  attnfp4::BwdParams p;
+  p.q_codes = (const uint8_t*)a->q_codes;
+  p.q_scales = (const uint8_t*)a->q_scales;
+  p.k_codes = (const uint8_t*)a->k_codes;
+  p.k_scales = (const uint8_t*)a->k_scales;
+  p.v_codes = (const uint8_t*)a->v_codes;
+  p.v_scales = (const uint8_t*)a->v_scales;
+  p.o = (const uint16_t*)a->o;
+  p.dout = (const uint16_t*)a->do_;
+  p.m = a->m;
+  p.l = a->l;
+  p.dq = (uint16_t*)a->dq;
+  p.dk = (uint16_t*)a->dk;
+  p.dv = (uint16_t*)a->dv;
+  p.delta = (float*)a->workspace;
+  p.dq_acc = (float*)((uint8_t*)a->workspace + ((a->B * a->Hq * a->N * 4 + 255) / 256) * 256);
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.N = a->N;
+  p.d = a->d;
+  p.causal = a->causal != 0;
+  const double s = resolve_scale(a->softmax_scale, a->d);
+  p.c = (float)(s * 1.4426950408889634);
+  p.scale_nat = (float)s;
+  hipError_t e = attnfp4::launch_bwd(p, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return ATTN_FP4_E_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal helpers shared by the gfx950 kernels of libattnfp4 (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfp4 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// E8M0 exponent of the MX block scale from the block's max magnitude (fp32 bits):
+// e = clamp(floor(log2 amax) - 2, -127, 127), with amax < 2^-126 counted as 2^-127.
+// For a finite fp32 amax the biased exponent field E gives floor(log2 amax) = E - 127
+// (E = 0 for zero and subnormals, which yields the -127 of the rule), so the scale
+// byte e + 127 is max(E - 2, 0).
+__device__ __forceinline__ int mx_scale_byte_from_amax_bits(uint32_t amax_bits) {
+  int field = (int)((amax_bits >> 23) & 0xFF);
+  return field > 2 ? field - 2 : 0;
+}
+
+// 2^k as an fp32 for k in [-126, 127].
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+}  // namespace attnfp4

@@ -1,0 +1,357 @@
+// MXFP4 FlashAttention-style forward for gfx950.
+//
+// The computation (Attn-QAT abstract: FP4 attention forward; HiFA4 abstract: QK^T and PV as
+// 4-bit GEMMs with a wider online-softmax state; EFQ-Softmax abstract: exp-then-quantize P, the
+// same quantized P in the PV numerator and the P.1 denominator, FlashAttention's running max,
+// history rescaling, wide accumulation and final normalisation):
+//   per query row, over ascending 64-key tiles:
+//     s = q^.k^ (raw, fp32 from the scaled FP4 MFMA),  m' = max(m, max s)
+//     p = exp(scale * (s - m')),  P~ = MXFP4(p) per 32-key block
+//     l = alpha l + sum P~,  acc = alpha acc + P~ V^,  alpha = exp(scale * (m - m'))
+//   O = acc / l (bf16), saved m (natural-log units) and l.
+//
+// gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
+// K^/V^ tile through LDS (double buffered, one barrier per tile).
+//  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
+//    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 32 rows of each
+//    S^T MFMA are loaded with a permutation of the keys chosen so that, in the MFMA's output
+//    layout, lane l holds 16 *consecutive* keys of query l%32: keys 32T + 16(l/32) + r in
+//    register r of tile T (T = 0, 1 covers the 64-key tile).
+//  * Each 32-key P block is therefore split over the lane pair (l, l+32).  Two permlane32
+//    swaps give both lanes the block maxima; each lane converts its 32 values with the hardware
+//    E2M1 conversion (v_cvt_scalef32_pk_fp4_f32); two more swaps of the packed codes leave lane l
+//    with the 32 consecutive keys of block l/32 for query l%32 -- exactly the B-operand layout of
+//    the scaled FP4 MFMA, with the block's E8M0 scale as that lane's B scale.
+//  * O is accumulated transposed, O^T = V^T P~^T (A = V^ in its transposed [d, N] layout from
+//    LDS, B = the packed P~), so each lane's accumulators belong to one query and the history
+//    rescale needs no cross-lane traffic.
+//  * The denominator sum of P~ runs on the matrix core too: one 16x16x128 scaled MFMA with a
+//    constant 0/1 A operand reduces the same packed P~ registers to per-query row sums.
+#include "common.h"
+#include "internal.h"
+
+namespace attnfp4 {
+
+namespace {
+
+constexpr int BC = 64;  // key-tile width; part of the definition of P quantization
+
+// Key held by row r (0..31) of an S^T MFMA tile: r = 8a + 4b + c -> key 16b + 4a + c.  With the
+// 32x32 MFMA output layout (register i of lane l is row 8(i/4) + 4(l/32) + i%4) this puts key
+// 16(l/32) + i in register i of lane l.
+__device__ __forceinline__ int row_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+template <int D>
+struct Stage {
+  static constexpr int KC_BYTES = BC * D / 2;   // K^ codes of one tile
+  static constexpr int KS_BYTES = BC * 4;       // K^ scales, one dword per key
+  static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2]
+  static constexpr int VS_BYTES = D * 2;        // V^ scales, two blocks per channel
+  static constexpr int KC = 0;
+  static constexpr int KS = KC + KC_BYTES;
+  static constexpr int VC = KS + KS_BYTES;
+  static constexpr int VS = VC + VC_BYTES;
+  static constexpr int BYTES = VS + VS_BYTES;
+  static constexpr int KCHUNKS = D / 32;        // 16-byte chunks per K^ row
+};
+
+__device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+
+template <int D, int W, bool CAUSAL>
+__global__ void __launch_bounds__(64 * W) fwd_kernel(FwdParams p) {
+  using S = Stage<D>;
+  constexpr int NT = 64 * W;                      // threads
+  constexpr int KS_STEPS = D / 64;                // MFMA k-steps over the head dim
+  constexpr int CT = D / 32;                      // 32-channel output tiles
+  constexpr int NKCH = BC * S::KCHUNKS;           // K^ code chunks per tile
+  constexpr int NVCH = D * 2;                     // V^ code chunks per tile
+  constexpr int KPT = (NKCH + NT - 1) / NT;
+  constexpr int VPT = (NVCH + NT - 1) / NT;
+  constexpr int NSC = BC + D;                     // scale loads per tile (K dwords + V halves)
+  constexpr int SPT = (NSC + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][S::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- work item: XCD-aware remap so that the workgroups of one head run on one XCD ----
+  const int64_t nqt = p.N / (32 * W);
+  const int64_t total = nqt * p.Hq * p.B;
+  int64_t id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const int64_t bh = id / nqt;
+  int64_t qt = id - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;                  // longest rows first
+  const int64_t b = bh / p.Hq;
+  const int64_t h = bh - b * p.Hq;
+  const int64_t g = h / (p.Hq / p.Hkv);
+  const int64_t N = p.N;
+  const int64_t q0 = qt * 32 * W;
+  const int64_t qw = q0 + 32 * wave;
+  const int64_t row = qw + l32;
+
+  const uint8_t* kcg = p.k_codes + (b * p.Hkv + g) * N * (D / 2);
+  const uint8_t* ksg = p.k_scales + (b * p.Hkv + g) * N * (D / 32);
+  const uint8_t* vcg = p.v_codes + (b * p.Hkv + g) * D * (N / 2);
+  const uint8_t* vsg = p.v_scales + (b * p.Hkv + g) * D * (N / 32);
+
+  // ---- the wave's Q^ as the B operand of S^T = K^ Q^T (fixed for the whole kernel) ----
+  v8i qb[KS_STEPS];
+  int qsc;
+  {
+    const uint8_t* qr = p.q_codes + ((b * p.Hq + h) * N + row) * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = widen(*reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks));
+    const uint8_t* qs = p.q_scales + ((b * p.Hq + h) * N + row) * (D / 32);
+    qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 8)) : (int)qs[hi];
+  }
+
+  // constant A operand of the row-sum MFMA (16x16x128): row 0 sums the K-blocks holding query
+  // l%16 (lanes 0-15 and 32-47), row 1 those holding query l%16 + 16 (lanes 16-31, 48-63)
+  v8i ones_a;
+  {
+    const int r16 = lane & 15, kb = lane >> 4;
+    const int on = (r16 == 0 && (kb & 1) == 0) || (r16 == 1 && (kb & 1) == 1);
+    const int v = on ? 0x22222222 : 0;           // E2M1 code 2 = 1.0
+    ones_a = v8i{v, v, v, v, 0, 0, 0, 0};
+  }
+
+  v16f o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = v16f{};
+  v4f lsum = v4f{};
+  float m_run = -__builtin_inff();
+  const float c = p.c;
+
+  // ---- tile range ----
+  const int64_t ntiles = CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC);
+
+  // ---- global -> register staging of one tile ----
+  v4i kreg[KPT], vreg[VPT];
+  uint32_t sreg[SPT];
+  auto load_tile = [&](int64_t t) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < NKCH) {
+        const int s = ci / S::KCHUNKS, cc = ci % S::KCHUNKS;
+        const int key = 32 * (s >> 5) + row_key(s & 31);
+        kreg[i] = *reinterpret_cast<const v4i*>(kcg + (t * BC + key) * (D / 2) + 16 * cc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < NVCH) {
+        const int ch = ci >> 1, cc = ci & 1;
+        vreg[i] = *reinterpret_cast<const v4i*>(vcg + ch * (N / 2) + t * (BC / 2) + 16 * cc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int si = tid + i * NT;
+      if (si < BC) {
+        const int key = 32 * (si >> 5) + row_key(si & 31);
+        if (D == 128) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(ksg + (t * BC + key) * 4);
+          // [b0, b1, b2, b3] -> [b0, b2, b1, b3]: lane half h then reads (b_h, b_{2+h}) as a u16
+          sreg[i] = (w & 0xFF0000FFu) | ((w >> 8) & 0x0000FF00u) | ((w << 8) & 0x00FF0000u);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint16_t*>(ksg + (t * BC + key) * 2);
+          sreg[i] = (w & 0xFFu) | ((w & 0xFF00u) << 8);   // [b0, 0, b1, 0]
+        }
+      } else if (si < NSC) {
+        const int ch = si - BC;
+        sreg[i] = *reinterpret_cast<const uint16_t*>(vsg + ch * (N / 32) + 2 * t);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint8_t* base = smem[st];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < NKCH) {
+        const int s = ci / S::KCHUNKS, cc = ci % S::KCHUNKS;
+        const int pc = cc ^ ((s >> 1) & (S::KCHUNKS - 1));
+        *reinterpret_cast<v4i*>(base + S::KC + s * (D / 2) + 16 * pc) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int ci = tid + i * NT;
+      if (ci < NVCH) {
+        const int ch = ci >> 1, cc = ci & 1;
+        const int pc = cc ^ ((ch >> 2) & 1);
+        *reinterpret_cast<v4i*>(base + S::VC + ch * 32 + 16 * pc) = vreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int si = tid + i * NT;
+      if (si < BC) {
+        *reinterpret_cast<uint32_t*>(base + S::KS + 4 * si) = sreg[i];
+      } else if (si < NSC) {
+        *reinterpret_cast<uint16_t*>(base + S::VS + 2 * (si - BC)) = (uint16_t)sreg[i];
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int st = (int)(t & 1);
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+
+    // a causal wave visits tile t only if its last row reaches the tile's first key; rows of a
+    // wave are 32-aligned and tiles 64-aligned, so the wave's rows all visit or all skip
+    const bool active = !CAUSAL || (t * BC <= qw + 31);
+    if (active) {
+      const uint8_t* base = smem[st];
+      // ---- S^T = K^ Q^T, two 32-key tiles ----
+      v16f sT[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int s = 32 * T + l32;
+        const int ksc = *reinterpret_cast<const uint16_t*>(base + S::KS + 4 * s + 2 * hi);
+        v16f acc = v16f{};
+#pragma unroll
+        for (int ks = 0; ks < KS_STEPS; ++ks) {
+          const int pc = (hi + 2 * ks) ^ ((s >> 1) & (S::KCHUNKS - 1));
+          const v4i ka = *reinterpret_cast<const v4i*>(base + S::KC + s * (D / 2) + 16 * pc);
+          if (ks == 0)
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), qb[0], acc, 4, 4, 0, ksc, 0, qsc);
+          else
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), qb[KS_STEPS - 1], acc, 4, 4, 1, ksc, 1, qsc);
+        }
+        sT[T] = acc;
+      }
+      // ---- causal mask on the diagonal tiles: key j > row i -> -inf ----
+      if (CAUSAL && (t * BC + BC - 1 > qw)) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t j = t * BC + 32 * T + 16 * hi + r;
+            if (j > row) sT[T][r] = -__builtin_inff();
+          }
+      }
+      // ---- block maxima (raw scores) ----
+      float mx0 = sT[0][0], mx1 = sT[1][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        mx0 = fmaxf(mx0, sT[0][r]);
+        mx1 = fmaxf(mx1, sT[1][r]);
+      }
+      // lanes l and l+32 hold the two halves of each block
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
+      const float bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
+      const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      // ---- E8M0 scale of each P block from its max: p_max = exp2((bmax - m) c); the row's own
+      //      maximum gives exactly exp2(0) = 1.  Exponents below -126 are clamped (P < 2^-124) ----
+      const float pm0 = __builtin_amdgcn_exp2f((bmax0 - m_new) * c);
+      const float pm1 = __builtin_amdgcn_exp2f((bmax1 - m_new) * c);
+      const int sb0 = max((int)((__float_as_uint(pm0) >> 23) & 0xFF) - 2, 1);
+      const int sb1 = max((int)((__float_as_uint(pm1) >> 23) & 0xFF) - 2, 1);
+      const float sc0 = __uint_as_float((uint32_t)sb0 << 23);
+      const float sc1 = __uint_as_float((uint32_t)sb1 << 23);
+      // ---- p = exp2(s c - m c) and E2M1 conversion against the block scale ----
+      const float mc = m_new * c;
+      uint32_t pk[2][2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const float sc = T == 0 ? sc0 : sc1;
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
+          uint32_t u = 0;
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[4], e[5], sc, 2);
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[6], e[7], sc, 3);
+          pk[T][hw] = u;
+        }
+      }
+      // regroup: lane l gets the 32 consecutive keys of block l/32 (tile T = l/32)
+      auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+      auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+      const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
+      const int psc = hi ? sb1 : sb0;
+
+      // ---- history rescale (skipped when no row of the wave raised its max) ----
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+        auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+        lsum[0] *= alpha;
+        lsum[1] *= __uint_as_float(ah[1]);
+      }
+      // ---- l += sum P~ (matrix core) and acc += P~ V^ ----
+      lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones_a, pb, lsum, 4, 4, 0, 127, 0, psc);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int ch = 32 * ct + l32;
+        const int pc = hi ^ ((ch >> 2) & 1);
+        const v4i va = *reinterpret_cast<const v4i*>(base + S::VC + ch * 32 + 16 * pc);
+        const int vsc = base[S::VS + 2 * ch + hi];
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(va), pb, o[ct], 4, 4, 0, vsc, 0, psc);
+      }
+    }
+
+    if (more) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: gather l per query, normalise, store O (bf16), m, l ----
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum[0]), __float_as_uint(lsum[1]), false, false);
+  auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[0], false, false);
+  const float lrow = __uint_as_float(r32[0]);
+  const float inv = 1.0f / lrow;
+  uint16_t* orow = p.o + ((b * p.Hq + h) * N + row) * D;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = 32 * ct + 8 * a + 4 * hi;
+      uint2 w;
+      w.x = pack_bf16x2(o[ct][4 * a + 0] * inv, o[ct][4 * a + 1] * inv);
+      w.y = pack_bf16x2(o[ct][4 * a + 2] * inv, o[ct][4 * a + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + ch) = w;
+    }
+  if (hi == 0) {
+    p.m[(b * p.Hq + h) * N + row] = m_run * p.scale_nat;
+    p.l[(b * p.Hq + h) * N + row] = lrow;
+  }
+}
+
+template <int D, int W, bool CAUSAL>
+hipError_t launch(const FwdParams& p, hipStream_t stream) {
+  const int64_t blocks = (p.N / (32 * W)) * p.Hq * p.B;
+  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  // the host layer guarantees N % 64 == 0; a workgroup of 2 waves covers 64 rows
+  if (d == 128) return causal ? launch<128, 2, true>(p, stream) : launch<128, 2, false>(p, stream);
+  return causal ? launch<64, 2, true>(p, stream) : launch<64, 2, false>(p, stream);
+}
+
+}  // namespace attnfp4

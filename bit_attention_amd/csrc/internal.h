@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer and the kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfp4 {
+
+struct FwdParams {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  uint16_t* o;
+  float* m;
+  float* l;
+  int64_t B, Hq, Hkv, N;
+  float c;          // softmax_scale * log2(e): raw score -> base-2 exponent
+  float scale_nat;  // softmax_scale: raw score -> natural-log units (saved m)
+};
+
+struct BwdParams {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* m;
+  const float* l;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;     // workspace: D = rowsum(dO * O), [B, Hq, N]
+  float* dq_acc;    // workspace: fp32 dQ accumulator, [B, Hq, N, d]
+  int64_t B, Hq, Hkv, N, d;
+  int causal;
+  float c;
+  float scale_nat;
+};
+
+hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
+                           void* scales, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
+int64_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace attnfp4

@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libattnfp4.so (same entry-point names as include/attn_fp4.h).
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+If the library is missing or fails to load, every call raises -- there is no
+fallback path.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnfp4.so")
+
+STATUS = {
+    0: "ATTN_FP4_OK",
+    1: "ATTN_FP4_E_INVALID_ARG",
+    2: "ATTN_FP4_E_UNSUPPORTED_DEVICE",
+    3: "ATTN_FP4_E_UNSUPPORTED",
+    4: "ATTN_FP4_E_HIP",
+    5: "ATTN_FP4_E_WORKSPACE",
+}
+
+EXPORTED = (
+    "attn_fp4_abi_version",
+    "attn_fp4_status_string",
+    "attn_fp4_quantize",
+    "attn_fp4_fwd",
+    "attn_fp4_bwd_workspace_bytes",
+    "attn_fp4_bwd_recompute",
+)
+
+
+class AttnFp4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (what, STATUS.get(status, status), _status_string(status)))
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_codes", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("N", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_codes", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("do_", ctypes.c_void_p),
+        ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("N", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libattnfp4.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libattnfp4.so is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.attn_fp4_abi_version.restype = ctypes.c_int32
+        L.attn_fp4_status_string.restype = ctypes.c_char_p
+        L.attn_fp4_status_string.argtypes = [ctypes.c_int32]
+        L.attn_fp4_quantize.restype = ctypes.c_int32
+        L.attn_fp4_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_fp4_fwd.restype = ctypes.c_int32
+        L.attn_fp4_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.attn_fp4_bwd_workspace_bytes.restype = ctypes.c_int64
+        L.attn_fp4_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 5
+        L.attn_fp4_bwd_recompute.restype = ctypes.c_int32
+        L.attn_fp4_bwd_recompute.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def _status_string(status):
+    try:
+        return lib().attn_fp4_status_string(status).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(status, what):
+    if status != 0:
+        raise AttnFp4Error(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+
+
+def attn_fp4_abi_version():
+    return int(lib().attn_fp4_abi_version())
+
+
+def attn_fp4_quantize(x, axis, codes=None, scales=None, stream=None):
+    """MXFP4-quantize bf16 ``x`` [..., n, d].
+
+    axis=0: along d -> codes [..., n, d/2], scales [..., n, d/32] (uint8).
+    axis=1: along n, transposed -> codes [..., d, n/2], scales [..., d, n/32].
+    """
+    _dev(x, torch.bfloat16, "x")
+    *lead, n, d = x.shape
+    bh = int(math.prod(lead)) if lead else 1
+    if axis == 0:
+        cshape, sshape = (*lead, n, d // 2), (*lead, n, d // 32)
+    else:
+        cshape, sshape = (*lead, d, n // 2), (*lead, d, n // 32)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _check(lib().attn_fp4_quantize(_ptr(x), bh, n, d, int(axis), _ptr(codes), _ptr(scales), _stream(stream)),
+           "attn_fp4_quantize")
+    return codes, scales
+
+
+def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal=False,
+                 softmax_scale=0.0, o=None, m=None, l=None, stream=None):
+    """MXFP4 attention forward on pre-quantized operands (layouts of attn_fp4_quantize).
+
+    q_codes [B, Hq, N, d/2]; k_codes [B, Hkv, N, d/2]; v_codes [B, Hkv, d, N/2].
+    Returns (o bf16 [B, Hq, N, d], m fp32 [B, Hq, N], l fp32 [B, Hq, N]).
+    """
+    B, Hq, N, dh = q_codes.shape
+    d = 2 * dh
+    Hkv = k_codes.shape[1]
+    for t, name in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
+                    (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, torch.uint8, name)
+    if k_codes.shape != (B, Hkv, N, dh) or v_codes.shape != (B, Hkv, d, N // 2):
+        raise ValueError("inconsistent operand shapes")
+    if q_scales.shape != (B, Hq, N, d // 32) or k_scales.shape != (B, Hkv, N, d // 32) \
+            or v_scales.shape != (B, Hkv, d, N // 32):
+        raise ValueError("inconsistent scale shapes")
+    dev = q_codes.device
+    if o is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    if m is None:
+        m = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    a = FwdArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale))
+    _check(lib().attn_fp4_fwd(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd")
+    return o, m, l
+
+
+def attn_fp4_bwd_workspace_bytes(B, Hq, Hkv, N, d):
+    return int(lib().attn_fp4_bwd_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def attn_fp4_bwd_recompute(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, o, do, m, l,
+                           causal=False, softmax_scale=0.0, dq=None, dk=None, dv=None, workspace=None,
+                           stream=None):
+    """Attn-QAT backward: returns (dq, dk, dv) bf16."""
+    B, Hq, N, dh = q_codes.shape
+    d = 2 * dh
+    Hkv = k_codes.shape[1]
+    dev = q_codes.device
+    _dev(o, torch.bfloat16, "o")
+    _dev(do, torch.bfloat16, "do")
+    _dev(m, torch.float32, "m")
+    _dev(l, torch.float32, "l")
+    if dq is None:
+        dq = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    if dk is None:
+        dk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    if dv is None:
+        dv = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    need = attn_fp4_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if need < 0:
+        raise AttnFp4Error(1, "attn_fp4_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    a = BwdArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                _ptr(o), _ptr(do), _ptr(m), _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale))
+    _check(lib().attn_fp4_bwd_recompute(ctypes.byref(a), _stream(stream)), "attn_fp4_bwd_recompute")
+    return dq, dk, dv

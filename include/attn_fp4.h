@@ -1,0 +1,175 @@
+/*
+ * attn_fp4.h -- C ABI of libattnfp4.so: 4-bit (MXFP4) FlashAttention-style
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *  - Attn-QAT: 4-Bit Attention With Quantization-Aware Training (abstract):
+ *    an FP4 attention forward, and a backward that recomputes the attention
+ *    scores with the same low-precision QK^T and takes the D term of the
+ *    FlashAttention gradient from the FP4 forward's own output.
+ *  - EFQ-Softmax abstract (AVQ Attention page; theflow "related" summary):
+ *    the FlashAttention-style data flow with block-scaled E2M1 probabilities
+ *    produced by the exp-then-quantize path, where one quantized P feeds both
+ *    the PV numerator and the P.1 denominator, while the row-max update,
+ *    historical rescaling, wide accumulation and final normalisation are
+ *    those of FlashAttention.
+ *  - HiFA4 abstract (theflow "related" page): QK^T and PV both run as 4-bit
+ *    GEMMs with the online-softmax state kept wider (fp32 here).
+ *
+ * Number format (MXFP4, OCP Microscaling reading of "microscaling FP4"):
+ *  - E2M1 code, 4 bits: bit 3 sign, magnitudes {0,.5,1,1.5,2,3,4,6} for
+ *    codes 0..7; two codes per byte, element 2c in bits 3..0 and element
+ *    2c+1 in bits 7..4.
+ *  - E8M0 scale, 1 byte per 32 consecutive elements of the contraction
+ *    axis: value 2^(byte-127); byte = clamp(floor(log2 amax) - 2, -127, 127)
+ *    + 127 (amax < 2^-126 counts as 2^-127); 0xFF is never written.
+ *  - element code = round-to-nearest-even of x / 2^(byte-127) onto the
+ *    grid, ties to the even code, saturating at 6, sign kept (-0 -> 0x8).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors on ROCm), contiguous, row-major, 16-byte aligned.  The caller
+ *    owns and allocates every buffer; the library never allocates, frees,
+ *    synchronises or keeps state beyond a cached per-device arch check.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; nothing is waited for.
+ *  - Every function returns an attn_fp4_status; argument errors are
+ *    detected on the host before anything is launched.  No exceptions cross
+ *    the ABI, nothing is printed, nothing aborts.
+ *  - Preconditions that are not checked: inputs finite; output buffers do
+ *    not overlap inputs or each other.
+ *  - Key-tile width: the forward visits keys in ascending tiles of 64 and
+ *    quantizes P per row over the tile's two 32-key blocks against the
+ *    running maximum after that tile; N must therefore be a multiple of 64.
+ */
+#ifndef ATTN_FP4_H
+#define ATTN_FP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_FP4_OK = 0,
+  ATTN_FP4_E_INVALID_ARG = 1,        /* null/misaligned pointer, bad shape, bad enum value */
+  ATTN_FP4_E_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950 */
+  ATTN_FP4_E_UNSUPPORTED = 3,        /* valid request this build does not implement */
+  ATTN_FP4_E_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+  ATTN_FP4_E_WORKSPACE = 5           /* workspace missing or smaller than required */
+} attn_fp4_status;
+
+/* Version of this ABI (structs and semantics); bumped on any change. */
+int32_t attn_fp4_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* attn_fp4_status_string(int32_t status);
+
+/*
+ * attn_fp4_quantize -- bf16 -> MXFP4 (packed E2M1 codes + E8M0 scales).
+ *
+ * Follows the block-scaled E2M1 operand format of the EFQ-Softmax abstract
+ * and the microscaling FP4 of the SageAttention3 title (Pengle Zhang page).
+ *
+ *   x       bf16 [bh, n, d], device.
+ *   axis 0  quantize along d (Q and K): codes [bh, n, d/2] bytes,
+ *           scales [bh, n, d/32] bytes.  Requires d % 32 == 0.
+ *   axis 1  quantize along n (V), written transposed so that keys are the
+ *           contiguous axis: codes [bh, d, n/2], scales [bh, d, n/32].
+ *           Requires n % 32 == 0 and d % 32 == 0 (d % 32 for the transpose).
+ *   bh, n, d > 0.  Output is bit-exact with the rule in the header comment.
+ * Errors: ATTN_FP4_E_INVALID_ARG for null or non-16-byte-aligned pointers,
+ * non-positive sizes, a length not divisible as required, axis not 0/1.
+ */
+int32_t attn_fp4_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32_t axis,
+                          void* codes, void* scales, void* stream);
+
+/*
+ * Forward arguments.  Layouts (all device, contiguous):
+ *   q_codes [B, Hq, N, d/2]   q_scales [B, Hq, N, d/32]   (attn_fp4_quantize axis 0)
+ *   k_codes [B, Hkv, N, d/2]  k_scales [B, Hkv, N, d/32]  (axis 0)
+ *   v_codes [B, Hkv, d, N/2]  v_scales [B, Hkv, d, N/32]  (axis 1, transposed)
+ *   o       bf16 [B, Hq, N, d]            (output, round-to-nearest-even)
+ *   m       fp32 [B, Hq, N]  final row max of the scaled scores (natural-log
+ *                            units, i.e. of s = scale * q.k)        (output)
+ *   l       fp32 [B, Hq, N]  final row sum of the quantized P      (output)
+ * Query head h reads KV head h / (Hq / Hkv).  causal != 0 masks keys j > i
+ * (top-left aligned, equal query and key lengths).  softmax_scale <= 0
+ * selects 1/sqrt(d).  Supported: d == 128 or d == 64, N % 64 == 0,
+ * Hq % Hkv == 0.
+ */
+typedef struct {
+  const void* q_codes;
+  const void* q_scales;
+  const void* k_codes;
+  const void* k_scales;
+  const void* v_codes;
+  const void* v_scales;
+  void* o;
+  float* m;
+  float* l;
+  int64_t B, Hq, Hkv, N, d;
+  int32_t causal;
+  float softmax_scale;
+} attn_fp4_fwd_args;
+
+/*
+ * attn_fp4_fwd -- MXFP4 attention forward (Attn-QAT FP4 forward; EFQ-Softmax
+ * exp-then-quantize data flow; HiFA4 4-bit QK^T and PV).  Both GEMMs run
+ * on the scaled FP4 matrix cores; the running max, running sum and the
+ * output accumulator are fp32.  Bitwise deterministic.
+ * Errors: ATTN_FP4_E_INVALID_ARG (null/misaligned pointer, bad dims),
+ * ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP (launch failure).
+ */
+int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
+
+/*
+ * Backward arguments.  Quantized operands as for the forward; o, m, l are
+ * the forward's outputs; do_ is bf16 [B, Hq, N, d].  Outputs dq bf16
+ * [B, Hq, N, d], dk and dv bf16 [B, Hkv, N, d] (summed over the query heads
+ * that share a KV head).  workspace: device memory of at least
+ * attn_fp4_bwd_workspace_bytes(...) bytes, 256-byte aligned; its contents
+ * on entry do not matter and are clobbered.
+ */
+typedef struct {
+  const void* q_codes;
+  const void* q_scales;
+  const void* k_codes;
+  const void* k_scales;
+  const void* v_codes;
+  const void* v_scales;
+  const void* o;
+  const void* do_;
+  const float* m;
+  const float* l;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  int64_t workspace_bytes;
+  int64_t B, Hq, Hkv, N, d;
+  int32_t causal;
+  float softmax_scale;
+} attn_fp4_bwd_args;
+
+/* Workspace bytes attn_fp4_bwd_recompute needs for these sizes (< 0 on invalid sizes). */
+int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
+
+/*
+ * attn_fp4_bwd_recompute -- Attn-QAT backward (abstract's two principles):
+ * S is recomputed with the same FP4 QK^T as the forward; D = rowsum(dO*O)
+ * uses the FP4 forward's output O (fp32); P = exp(S - m)/l; the dV operand
+ * is the requantized P (MXFP4 of exp(S - m) per 32-key block, divided by
+ * l); dQ, dK, dV come from bf16 matrix-core products with fp32
+ * accumulation, gradients passing straight through the quantizers.
+ * Errors: as attn_fp4_fwd, plus ATTN_FP4_E_WORKSPACE, and
+ * ATTN_FP4_E_UNSUPPORTED for combinations this build does not implement.
+ */
+int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FP4_H */

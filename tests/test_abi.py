@@ -1,0 +1,69 @@
+"""The C-ABI library loads and exports every symbol include/attn_fp4.h declares (CPU only).
+
+Only host-side argument validation is exercised here: every call below is rejected before
+anything touches a device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_attention_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(attn_fp4_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(ops.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert ops.attn_fp4_abi_version() == 1
+
+
+def test_status_strings():
+    L = ops.lib()
+    for s in range(6):
+        assert L.attn_fp4_status_string(s)
+    assert L.attn_fp4_status_string(99) == b"unknown status"
+
+
+def test_host_validation_rejects_before_launch():
+    L = ops.lib()
+    # null / misaligned pointers and bad sizes are rejected on the host
+    assert L.attn_fp4_quantize(None, 1, 32, 32, 0, None, None, None) == 1
+    assert L.attn_fp4_quantize(ctypes.c_void_p(16), 1, 32, 33, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 1
+    assert L.attn_fp4_quantize(ctypes.c_void_p(16), 1, 32, 32, 2, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 1
+    assert L.attn_fp4_quantize(ctypes.c_void_p(8), 1, 32, 32, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 1
+    a = ops.FwdArgs()
+    assert L.attn_fp4_fwd(None, None) == 1
+    assert L.attn_fp4_fwd(ctypes.byref(a), None) == 1          # zero dims
+    p = ctypes.c_void_p(256)
+    for kw in ({"N": 96}, {"d": 96}, {"Hkv": 3}):
+        dims = dict(B=1, Hq=4, Hkv=2, N=128, d=128)
+        dims.update(kw)
+        a = ops.FwdArgs(p, p, p, p, p, p, p, p, p, dims["B"], dims["Hq"], dims["Hkv"], dims["N"], dims["d"], 0, 0.0)
+        assert L.attn_fp4_fwd(ctypes.byref(a), None) == 1, kw
+    assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 1024 + 128 * 128 * 2 * 4
+    assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0
+    b = ops.BwdArgs(p, p, p, p, p, p, p, p, p, p, p, p, p, None, 0, 1, 2, 2, 128, 128, 0, 0.0)
+    assert L.attn_fp4_bwd_recompute(ctypes.byref(b), None) == 5   # workspace missing
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", "/nonexistent/libattnfp4.so")
+    with pytest.raises(RuntimeError):
+        ops.lib()

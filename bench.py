@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fwd-only-reps", type=int, default=0,
                     help="if > 0: only run the forward kernel this many times (for profilers)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="if > 0: only run a plain device copy of this many bytes 3 times "
+                         "(calibrates the HBM byte counters of a profiler)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -147,6 +150,16 @@ def main():
     import torch
     from bit_attention_amd import ops
     from bit_attention_amd import workloads as W
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes 3 times" % (src.numel() * 4))
+        return
 
     w = W.WORKLOADS["dit_b1h24n32768d128"]
     log("generating inputs for", w.name)

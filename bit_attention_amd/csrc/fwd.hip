@@ -11,7 +11,8 @@
 //   O = acc / l (bf16), saved m (natural-log units) and l.
 //
 // gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
-// K^/V^ tile through LDS (double buffered, one barrier per tile).
+// K^/V^ tile through LDS (three stages: the tile being finished, the next tile whose S is
+// already on the matrix core, and the one arriving from memory; one barrier per tile).
 //  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
 //    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 32 rows of each
 //    S^T MFMA are loaded with a permutation of the keys chosen so that, in the MFMA's output
@@ -27,6 +28,8 @@
 //    rescale needs no cross-lane traffic.
 //  * The denominator sum of P~ runs on the matrix core too: one 16x16x128 scaled MFMA with a
 //    constant 0/1 A operand reduces the same packed P~ registers to per-query row sums.
+//  * Software pipeline: the S^T MFMAs of tile t+1 are issued before the softmax VALU work of
+//    tile t, so the matrix core and the vector ALU work on different tiles of the same wave.
 #include "common.h"
 #include "internal.h"
 
@@ -43,8 +46,8 @@ __device__ __forceinline__ int row_key(int r) { return 16 * ((r >> 2) & 1) + 4 *
 
 template <int D>
 struct Stage {
-  static constexpr int KC_BYTES = BC * D / 2;   // K^ codes of one tile
-  static constexpr int KS_BYTES = BC * 4;       // K^ scales, one dword per key
+  static constexpr int KC_BYTES = BC * D / 2;   // K^ codes of one tile, [slot][d/2]
+  static constexpr int KS_BYTES = BC * 4;       // K^ scales, one dword per slot (d/32 <= 4 bytes)
   static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2]
   static constexpr int VS_BYTES = D * 2;        // V^ scales, two blocks per channel
   static constexpr int KC = 0;
@@ -58,19 +61,21 @@ struct Stage {
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
 template <int D, int W, bool CAUSAL>
-__global__ void __launch_bounds__(64 * W) fwd_kernel(FwdParams p) {
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_kernel(FwdParams p) {
   using S = Stage<D>;
   constexpr int NT = 64 * W;                      // threads
   constexpr int KS_STEPS = D / 64;                // MFMA k-steps over the head dim
   constexpr int CT = D / 32;                      // 32-channel output tiles
-  constexpr int NKCH = BC * S::KCHUNKS;           // K^ code chunks per tile
-  constexpr int NVCH = D * 2;                     // V^ code chunks per tile
+  constexpr int NKCH = BC * S::KCHUNKS;           // K^ code chunks (16 B) per tile
+  constexpr int NVCH = D * 2;                     // V^ code chunks (16 B) per tile
   constexpr int KPT = (NKCH + NT - 1) / NT;
   constexpr int VPT = (NVCH + NT - 1) / NT;
-  constexpr int NSC = BC + D;                     // scale loads per tile (K dwords + V halves)
+  constexpr int NSC = BC + D;                     // scale items per tile (K dwords, V u16)
   constexpr int SPT = (NSC + NT - 1) / NT;
+  constexpr int NSTAGE = 3;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,25 +105,137 @@ __global__ void __launch_bounds__(64 * W) fwd_kernel(FwdParams p) {
   const uint8_t* vsg = p.v_scales + (b * p.Hkv + g) * D * (N / 32);
 
   // ---- the wave's Q^ as the B operand of S^T = K^ Q^T (fixed for the whole kernel) ----
-  v8i qb[KS_STEPS];
+  v4i qb[KS_STEPS];
   int qsc;
   {
     const uint8_t* qr = p.q_codes + ((b * p.Hq + h) * N + row) * (D / 2);
 #pragma unroll
-    for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = widen(*reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks));
+    for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks);
     const uint8_t* qs = p.q_scales + ((b * p.Hq + h) * N + row) * (D / 32);
-    qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 8)) : (int)qs[hi];
+    qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 16)) : (int)qs[hi];
   }
 
   // constant A operand of the row-sum MFMA (16x16x128): row 0 sums the K-blocks holding query
   // l%16 (lanes 0-15 and 32-47), row 1 those holding query l%16 + 16 (lanes 16-31, 48-63)
-  v8i ones_a;
+  v4i ones_a;
   {
     const int r16 = lane & 15, kb = lane >> 4;
     const int on = (r16 == 0 && (kb & 1) == 0) || (r16 == 1 && (kb & 1) == 1);
     const int v = on ? 0x22222222 : 0;           // E2M1 code 2 = 1.0
-    ones_a = v8i{v, v, v, v, 0, 0, 0, 0};
+    ones_a = v4i{v, v, v, v};
   }
+
+  // ---- per-thread staging offsets (constant over tiles) ----
+  int kg_off[KPT], kl_off[KPT], vg_off[VPT], vl_off[VPT];
+  bool k_on[KPT], v_on[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int ci = tid + i * NT;
+    k_on[i] = ci < NKCH;
+    const int s = (ci / S::KCHUNKS) & (BC - 1), cc = ci % S::KCHUNKS;
+    const int key = 32 * (s >> 5) + row_key(s & 31);
+    kg_off[i] = key * (D / 2) + 16 * cc;
+    kl_off[i] = S::KC + s * (D / 2) + 16 * (cc ^ ((s >> 1) & (S::KCHUNKS - 1)));
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int ci = tid + i * NT;
+    v_on[i] = ci < NVCH;
+    const int ch = (ci >> 1) & (D - 1), cc = ci & 1;
+    vg_off[i] = ch * (int)(N / 2) + 16 * cc;
+    vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ ((ch >> 2) & 1));
+  }
+  int sg_kind[SPT], sg_off[SPT], sl_off[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int si = tid + i * NT;
+    if (si < BC) {
+      const int key = 32 * (si >> 5) + row_key(si & 31);
+      sg_kind[i] = 0;
+      sg_off[i] = key * (D / 32);
+      sl_off[i] = S::KS + 4 * si;
+    } else if (si < NSC) {
+      const int ch = si - BC;
+      sg_kind[i] = 1;
+      sg_off[i] = ch * (int)(N / 32);
+      sl_off[i] = S::VS + 2 * ch;
+    } else {
+      sg_kind[i] = 2;
+      sg_off[i] = 0;
+      sl_off[i] = 0;
+    }
+  }
+
+  // ---- per-lane LDS read offsets (constant over tiles) ----
+  // K^ A operand: slot 32T + l32, logical chunk hi + 2ks
+  int kr_off[KS_STEPS];
+#pragma unroll
+  for (int ks = 0; ks < KS_STEPS; ++ks)
+    kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ ((l32 >> 1) & (S::KCHUNKS - 1)));
+  const int ksr_off = S::KS + 4 * l32;
+  const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ ((l32 >> 2) & 1));
+  const int vsr_off = S::VS + 2 * l32 + hi;
+
+  v4i kreg[KPT], vreg[VPT];
+  uint32_t sreg[SPT];
+  auto load_tile = [&](int64_t t) {
+    const uint8_t* kt = kcg + t * (BC * D / 2);
+    const uint8_t* vt = vcg + t * (BC / 2);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (k_on[i]) kreg[i] = *reinterpret_cast<const v4i*>(kt + kg_off[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (v_on[i]) vreg[i] = *reinterpret_cast<const v4i*>(vt + vg_off[i]);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      if (sg_kind[i] == 0) {
+        const uint8_t* src = ksg + t * (BC * D / 32) + sg_off[i];
+        sreg[i] = (D == 128) ? *reinterpret_cast<const uint32_t*>(src)
+                             : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+      } else if (sg_kind[i] == 1) {
+        sreg[i] = *reinterpret_cast<const uint16_t*>(vsg + 2 * t + sg_off[i]);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint8_t* base = smem + st * S::BYTES;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (k_on[i]) *reinterpret_cast<v4i*>(base + kl_off[i]) = kreg[i];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (v_on[i]) *reinterpret_cast<v4i*>(base + vl_off[i]) = vreg[i];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      if (sg_kind[i] == 0)
+        *reinterpret_cast<uint32_t*>(base + sl_off[i]) = sreg[i];
+      else if (sg_kind[i] == 1)
+        *reinterpret_cast<uint16_t*>(base + sl_off[i]) = (uint16_t)sreg[i];
+    }
+  };
+
+  // ---- S^T = K^ Q^T for one tile (two 32-key halves) ----
+  auto compute_s = [&](int st, v16f* sT) {
+    const uint8_t* base = smem + st * S::BYTES;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      // the slot's d-block scales [b0 b1 b2 b3]; lane half hi needs block 2ks + hi
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
+      const int ksc = (int)(kw >> (8 * hi));     // byte 0: ks 0, byte 2: ks 1
+      v16f acc = v16f{};
+#pragma unroll
+      for (int ks = 0; ks < KS_STEPS; ++ks) {
+        const v4i ka = *reinterpret_cast<const v4i*>(base + kr_off[ks] + T * 32 * (D / 2));
+        if (ks == 0)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), acc, 4, 4, 0, ksc, 0, qsc);
+        else
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[KS_STEPS - 1]), acc, 4, 4, 2,
+                                                               ksc, 2, qsc);
+      }
+      sT[T] = acc;
+    }
+  };
 
   v16f o[CT];
 #pragma unroll
@@ -127,194 +244,116 @@ __global__ void __launch_bounds__(64 * W) fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   const float c = p.c;
 
-  // ---- tile range ----
-  const int64_t ntiles = CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC);
-
-  // ---- global -> register staging of one tile ----
-  v4i kreg[KPT], vreg[VPT];
-  uint32_t sreg[SPT];
-  auto load_tile = [&](int64_t t) {
+  // ---- softmax of one tile, P~ requantization, row sums and PV ----
+  auto softmax_pv = [&](int64_t t, int st, v16f* sT) {
+    const uint8_t* base = smem + st * S::BYTES;
+    if (CAUSAL && (t * BC + BC - 1 > qw)) {       // diagonal tile: key j > row i -> -inf
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < NKCH) {
-        const int s = ci / S::KCHUNKS, cc = ci % S::KCHUNKS;
-        const int key = 32 * (s >> 5) + row_key(s & 31);
-        kreg[i] = *reinterpret_cast<const v4i*>(kcg + (t * BC + key) * (D / 2) + 16 * cc);
-      }
-    }
+      for (int T = 0; T < 2; ++T)
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < NVCH) {
-        const int ch = ci >> 1, cc = ci & 1;
-        vreg[i] = *reinterpret_cast<const v4i*>(vcg + ch * (N / 2) + t * (BC / 2) + 16 * cc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int si = tid + i * NT;
-      if (si < BC) {
-        const int key = 32 * (si >> 5) + row_key(si & 31);
-        if (D == 128) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(ksg + (t * BC + key) * 4);
-          // [b0, b1, b2, b3] -> [b0, b2, b1, b3]: lane half h then reads (b_h, b_{2+h}) as a u16
-          sreg[i] = (w & 0xFF0000FFu) | ((w >> 8) & 0x0000FF00u) | ((w << 8) & 0x00FF0000u);
-        } else {
-          const uint32_t w = *reinterpret_cast<const uint16_t*>(ksg + (t * BC + key) * 2);
-          sreg[i] = (w & 0xFFu) | ((w & 0xFF00u) << 8);   // [b0, 0, b1, 0]
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = t * BC + 32 * T + 16 * hi + r;
+          if (j > row) sT[T][r] = -__builtin_inff();
         }
-      } else if (si < NSC) {
-        const int ch = si - BC;
-        sreg[i] = *reinterpret_cast<const uint16_t*>(vsg + ch * (N / 32) + 2 * t);
+    }
+    // block maxima of the raw scores; lanes l and l+32 hold the two halves of each block
+    float mx0 = sT[0][0], mx1 = sT[1][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      mx0 = fmaxf(mx0, sT[0][r]);
+      mx1 = fmaxf(mx1, sT[1][r]);
+    }
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
+    const float bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
+    const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    m_run = m_new;
+    // E8M0 scale of each P block from its max p = exp2((bmax - m) c); the row's own maximum gives
+    // exactly exp2(0) = 1.  Exponents below -126 are clamped (affects only P < 2^-124).
+    const float pm0 = __builtin_amdgcn_exp2f((bmax0 - m_new) * c);
+    const float pm1 = __builtin_amdgcn_exp2f((bmax1 - m_new) * c);
+    const int sb0 = max((int)(__float_as_uint(pm0) >> 23) - 2, 1);
+    const int sb1 = max((int)(__float_as_uint(pm1) >> 23) - 2, 1);
+    const float sc0 = __uint_as_float((uint32_t)sb0 << 23);
+    const float sc1 = __uint_as_float((uint32_t)sb1 << 23);
+    // p = exp2(s c - m c) and E2M1 conversion against the block scale
+    const float mc = m_new * c;
+    uint32_t pk[2][2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const float sc = T == 0 ? sc0 : sc1;
+#pragma unroll
+      for (int hw = 0; hw < 2; ++hw) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
+        uint32_t u = 0;
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[4], e[5], sc, 2);
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[6], e[7], sc, 3);
+        pk[T][hw] = u;
       }
+    }
+    // regroup: lane l gets the 32 consecutive keys of block l/32
+    auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+    auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+    const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
+    const int psc = hi ? sb1 : sb0;
+
+    // history rescale (skipped when no row of the wave raised its max)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+      auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+      lsum[0] *= alpha;
+      lsum[1] *= __uint_as_float(ah[1]);
+    }
+    // l += sum P~ (matrix core) and acc += P~ V^
+    lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(ones_a), pb, lsum, 4, 4, 0, 127, 0, psc);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const v4i va = *reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32);
+      const int vsc = base[vsr_off + ct * 64];
+      o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(va), pb, o[ct], 4, 4, 0, vsc, 0, psc);
     }
   };
-  auto store_tile = [&](int st) {
-    uint8_t* base = smem[st];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < NKCH) {
-        const int s = ci / S::KCHUNKS, cc = ci % S::KCHUNKS;
-        const int pc = cc ^ ((s >> 1) & (S::KCHUNKS - 1));
-        *reinterpret_cast<v4i*>(base + S::KC + s * (D / 2) + 16 * pc) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int ci = tid + i * NT;
-      if (ci < NVCH) {
-        const int ch = ci >> 1, cc = ci & 1;
-        const int pc = cc ^ ((ch >> 2) & 1);
-        *reinterpret_cast<v4i*>(base + S::VC + ch * 32 + 16 * pc) = vreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int si = tid + i * NT;
-      if (si < BC) {
-        *reinterpret_cast<uint32_t*>(base + S::KS + 4 * si) = sreg[i];
-      } else if (si < NSC) {
-        *reinterpret_cast<uint16_t*>(base + S::VS + 2 * (si - BC)) = (uint16_t)sreg[i];
-      }
-    }
-  };
+
+  // ---- tile loop ----
+  const int64_t ntiles = CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC);
+  auto active = [&](int64_t t) { return !CAUSAL || (t * BC <= qw + 31); };
 
   load_tile(0);
   store_tile(0);
+  if (ntiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
   __syncthreads();
 
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int st = (int)(t & 1);
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-
-    // a causal wave visits tile t only if its last row reaches the tile's first key; rows of a
-    // wave are 32-aligned and tiles 64-aligned, so the wave's rows all visit or all skip
-    const bool active = !CAUSAL || (t * BC <= qw + 31);
-    if (active) {
-      const uint8_t* base = smem[st];
-      // ---- S^T = K^ Q^T, two 32-key tiles ----
-      v16f sT[2];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const int s = 32 * T + l32;
-        const int ksc = *reinterpret_cast<const uint16_t*>(base + S::KS + 4 * s + 2 * hi);
-        v16f acc = v16f{};
-#pragma unroll
-        for (int ks = 0; ks < KS_STEPS; ++ks) {
-          const int pc = (hi + 2 * ks) ^ ((s >> 1) & (S::KCHUNKS - 1));
-          const v4i ka = *reinterpret_cast<const v4i*>(base + S::KC + s * (D / 2) + 16 * pc);
-          if (ks == 0)
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), qb[0], acc, 4, 4, 0, ksc, 0, qsc);
-          else
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), qb[KS_STEPS - 1], acc, 4, 4, 1, ksc, 1, qsc);
-        }
-        sT[T] = acc;
-      }
-      // ---- causal mask on the diagonal tiles: key j > row i -> -inf ----
-      if (CAUSAL && (t * BC + BC - 1 > qw)) {
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t j = t * BC + 32 * T + 16 * hi + r;
-            if (j > row) sT[T][r] = -__builtin_inff();
-          }
-      }
-      // ---- block maxima (raw scores) ----
-      float mx0 = sT[0][0], mx1 = sT[1][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        mx0 = fmaxf(mx0, sT[0][r]);
-        mx1 = fmaxf(mx1, sT[1][r]);
-      }
-      // lanes l and l+32 hold the two halves of each block
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
-      const float bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-      const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
-      const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      m_run = m_new;
-      // ---- E8M0 scale of each P block from its max: p_max = exp2((bmax - m) c); the row's own
-      //      maximum gives exactly exp2(0) = 1.  Exponents below -126 are clamped (P < 2^-124) ----
-      const float pm0 = __builtin_amdgcn_exp2f((bmax0 - m_new) * c);
-      const float pm1 = __builtin_amdgcn_exp2f((bmax1 - m_new) * c);
-      const int sb0 = max((int)((__float_as_uint(pm0) >> 23) & 0xFF) - 2, 1);
-      const int sb1 = max((int)((__float_as_uint(pm1) >> 23) & 0xFF) - 2, 1);
-      const float sc0 = __uint_as_float((uint32_t)sb0 << 23);
-      const float sc1 = __uint_as_float((uint32_t)sb1 << 23);
-      // ---- p = exp2(s c - m c) and E2M1 conversion against the block scale ----
-      const float mc = m_new * c;
-      uint32_t pk[2][2];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const float sc = T == 0 ? sc0 : sc1;
-#pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
-          uint32_t u = 0;
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[4], e[5], sc, 2);
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[6], e[7], sc, 3);
-          pk[T][hw] = u;
-        }
-      }
-      // regroup: lane l gets the 32 consecutive keys of block l/32 (tile T = l/32)
-      auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
-      auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
-      const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
-      const int psc = hi ? sb1 : sb0;
-
-      // ---- history rescale (skipped when no row of the wave raised its max) ----
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
-        auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
-        lsum[0] *= alpha;
-        lsum[1] *= __uint_as_float(ah[1]);
-      }
-      // ---- l += sum P~ (matrix core) and acc += P~ V^ ----
-      lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones_a, pb, lsum, 4, 4, 0, 127, 0, psc);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int ch = 32 * ct + l32;
-        const int pc = hi ^ ((ch >> 2) & 1);
-        const v4i va = *reinterpret_cast<const v4i*>(base + S::VC + ch * 32 + 16 * pc);
-        const int vsc = base[S::VS + 2 * ch + hi];
-        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(va), pb, o[ct], 4, 4, 0, vsc, 0, psc);
-      }
-    }
-
-    if (more) store_tile(st ^ 1);
+  v16f sA[2], sB[2];
+  if (active(0)) compute_s(0, sA);
+  int st_cur = 0, st_next = 1, st_pref = 2;
+  auto step = [&](int64_t t, v16f* cur, v16f* nxt) {
+    const bool pref = t + 2 < ntiles;
+    if (pref) load_tile(t + 2);
+    if (t + 1 < ntiles && active(t + 1)) compute_s(st_next, nxt);
+    if (active(t)) softmax_pv(t, st_cur, cur);
+    if (pref) store_tile(st_pref);
     __syncthreads();
+    const int tmp = st_cur;
+    st_cur = st_next;
+    st_next = st_pref;
+    st_pref = tmp;
+  };
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, sB, sA);
   }
 
   // ---- epilogue: gather l per query, normalise, store O (bf16), m, l ----
@@ -346,12 +385,17 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
+  // four waves (128 rows) per workgroup when the rows tile evenly, else two (N % 64 == 0)
+  if (p.N % 128 == 0) return causal ? launch<D, 4, true>(p, stream) : launch<D, 4, false>(p, stream);
+  return causal ? launch<D, 2, true>(p, stream) : launch<D, 2, false>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-  // the host layer guarantees N % 64 == 0; a workgroup of 2 waves covers 64 rows
-  if (d == 128) return causal ? launch<128, 2, true>(p, stream) : launch<128, 2, false>(p, stream);
-  return causal ? launch<64, 2, true>(p, stream) : launch<64, 2, false>(p, stream);
+  return d == 128 ? launch_d<128>(p, causal, stream) : launch_d<64>(p, causal, stream);
 }
 
 }  // namespace attnfp4

@@ -23,6 +23,7 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-fno-gpu-flush-denormals-to-zero",
+    "-fno-honor-nans",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

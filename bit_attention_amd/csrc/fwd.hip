@@ -72,14 +72,13 @@ fwd_kernel(FwdParams p) {
   constexpr int KPT = (NKCH + NT - 1) / NT;
   constexpr int VPT = (NVCH + NT - 1) / NT;
   constexpr int NSC = BC + D;                     // scale items per tile (K dwords, V u16)
-  constexpr int SPT = (NSC + NT - 1) / NT;
   constexpr int NSTAGE = 3;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -145,24 +144,25 @@ fwd_kernel(FwdParams p) {
     vg_off[i] = ch * (int)(N / 2) + 16 * cc;
     vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ ((ch >> 2) & 1));
   }
-  int sg_kind[SPT], sg_off[SPT], sl_off[SPT];
+  // scale items of a tile: 64 K^ dwords (one per slot), then D V^ u16 (two blocks per channel);
+  // in round r wave w stages items 64w + NT r + [0, 64), so the kind of item is uniform per wave
+  static_assert(NSC % 64 == 0 && NT % 64 == 0, "scale items come in whole waves");
+  constexpr int SR = (NSC + NT - 1) / NT;
+  int sg_off[SR], sl_off[SR];
+  bool s_is_k[SR], s_any[SR];
 #pragma unroll
-  for (int i = 0; i < SPT; ++i) {
-    const int si = tid + i * NT;
-    if (si < BC) {
-      const int key = 32 * (si >> 5) + row_key(si & 31);
-      sg_kind[i] = 0;
-      sg_off[i] = key * (D / 32);
-      sl_off[i] = S::KS + 4 * si;
-    } else if (si < NSC) {
-      const int ch = si - BC;
-      sg_kind[i] = 1;
-      sg_off[i] = ch * (int)(N / 32);
-      sl_off[i] = S::VS + 2 * ch;
+  for (int r = 0; r < SR; ++r) {
+    const int item = 64 * wave + lane + NT * r;
+    s_is_k[r] = 64 * wave + NT * r < BC;          // wave-uniform
+    s_any[r] = 64 * wave + NT * r < NSC;          // wave-uniform
+    if (s_is_k[r]) {
+      const int key = 32 * (item >> 5) + row_key(item & 31);
+      sg_off[r] = key * (D / 32);
+      sl_off[r] = S::KS + 4 * item;
     } else {
-      sg_kind[i] = 2;
-      sg_off[i] = 0;
-      sl_off[i] = 0;
+      const int ch = (item - BC) & (D - 1);
+      sg_off[r] = ch * (int)(N / 32);
+      sl_off[r] = S::VS + 2 * ch;
     }
   }
 
@@ -177,10 +177,10 @@ fwd_kernel(FwdParams p) {
   const int vsr_off = S::VS + 2 * l32 + hi;
 
   v4i kreg[KPT], vreg[VPT];
-  uint32_t sreg[SPT];
-  auto load_tile = [&](int64_t t) {
-    const uint8_t* kt = kcg + t * (BC * D / 2);
-    const uint8_t* vt = vcg + t * (BC / 2);
+  uint32_t sreg[SR];
+  auto load_tile = [&](int t) {
+    const uint8_t* kt = kcg + (int64_t)t * (BC * D / 2);
+    const uint8_t* vt = vcg + (int64_t)t * (BC / 2);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       if (k_on[i]) kreg[i] = *reinterpret_cast<const v4i*>(kt + kg_off[i]);
@@ -188,13 +188,14 @@ fwd_kernel(FwdParams p) {
     for (int i = 0; i < VPT; ++i)
       if (v_on[i]) vreg[i] = *reinterpret_cast<const v4i*>(vt + vg_off[i]);
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      if (sg_kind[i] == 0) {
-        const uint8_t* src = ksg + t * (BC * D / 32) + sg_off[i];
-        sreg[i] = (D == 128) ? *reinterpret_cast<const uint32_t*>(src)
+    for (int r = 0; r < SR; ++r) {
+      if (!s_any[r]) continue;
+      if (s_is_k[r]) {
+        const uint8_t* src = ksg + (int64_t)t * (BC * D / 32) + sg_off[r];
+        sreg[r] = (D == 128) ? *reinterpret_cast<const uint32_t*>(src)
                              : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
-      } else if (sg_kind[i] == 1) {
-        sreg[i] = *reinterpret_cast<const uint16_t*>(vsg + 2 * t + sg_off[i]);
+      } else {
+        sreg[r] = *reinterpret_cast<const uint16_t*>(vsg + 2 * t + sg_off[r]);
       }
     }
   };
@@ -207,33 +208,53 @@ fwd_kernel(FwdParams p) {
     for (int i = 0; i < VPT; ++i)
       if (v_on[i]) *reinterpret_cast<v4i*>(base + vl_off[i]) = vreg[i];
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      if (sg_kind[i] == 0)
-        *reinterpret_cast<uint32_t*>(base + sl_off[i]) = sreg[i];
-      else if (sg_kind[i] == 1)
-        *reinterpret_cast<uint16_t*>(base + sl_off[i]) = (uint16_t)sreg[i];
+    for (int r = 0; r < SR; ++r) {
+      if (!s_any[r]) continue;
+      if (s_is_k[r])
+        *reinterpret_cast<uint32_t*>(base + sl_off[r]) = sreg[r];
+      else
+        *reinterpret_cast<uint16_t*>(base + sl_off[r]) = (uint16_t)sreg[r];
     }
   };
 
-  // ---- S^T = K^ Q^T for one tile (two 32-key halves) ----
-  auto compute_s = [&](int st, v16f* sT) {
+  // ---- S^T = K^ Q^T for one tile (two 32-key halves); operands are read first, MFMAs later ----
+  struct KOps {
+    v4i a[2][KS_STEPS];
+    uint32_t w[2];
+  };
+  auto read_k = [&](int st, KOps& k) {
     const uint8_t* base = smem + st * S::BYTES;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       // the slot's d-block scales [b0 b1 b2 b3]; lane half hi needs block 2ks + hi
-      const uint32_t kw = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
-      const int ksc = (int)(kw >> (8 * hi));     // byte 0: ks 0, byte 2: ks 1
-      v16f acc = v16f{};
+      k.w[T] = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
 #pragma unroll
-      for (int ks = 0; ks < KS_STEPS; ++ks) {
-        const v4i ka = *reinterpret_cast<const v4i*>(base + kr_off[ks] + T * 32 * (D / 2));
-        if (ks == 0)
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), acc, 4, 4, 0, ksc, 0, qsc);
-        else
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[KS_STEPS - 1]), acc, 4, 4, 2,
-                                                               ksc, 2, qsc);
-      }
+      for (int ks = 0; ks < KS_STEPS; ++ks)
+        k.a[T][ks] = *reinterpret_cast<const v4i*>(base + kr_off[ks] + T * 32 * (D / 2));
+    }
+  };
+  auto mfma_s = [&](const KOps& k, v16f* sT) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int ksc = (int)(k.w[T] >> (8 * hi));   // byte 0: k-step 0, byte 2: k-step 1
+      v16f acc = v16f{};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(k.a[T][0]), widen(qb[0]), acc, 4, 4, 0, ksc, 0, qsc);
+      if (KS_STEPS == 2)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(k.a[T][KS_STEPS - 1]), widen(qb[KS_STEPS - 1]),
+                                                             acc, 4, 4, 2, ksc, 2, qsc);
       sT[T] = acc;
+    }
+  };
+  struct VOps {
+    v4i a[CT];
+    int s[CT];
+  };
+  auto read_v = [&](int st, VOps& v) {
+    const uint8_t* base = smem + st * S::BYTES;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      v.a[ct] = *reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32);
+      v.s[ct] = base[vsr_off + ct * 64];
     }
   };
 
@@ -244,51 +265,57 @@ fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   const float c = p.c;
 
-  // ---- softmax of one tile, P~ requantization, row sums and PV ----
-  auto softmax_pv = [&](int64_t t, int st, v16f* sT) {
-    const uint8_t* base = smem + st * S::BYTES;
+  // ---- online softmax, phase 1: mask, running max, block scales of P~ ----
+  struct Soft {
+    float mc, alpha, sc0, sc1;
+    int sb0, sb1;
+  };
+  auto softmax_max = [&](int t, v16f* sT, Soft& q) {
     if (CAUSAL && (t * BC + BC - 1 > qw)) {       // diagonal tile: key j > row i -> -inf
+      const int jrel = (int)(row - (int64_t)t * BC) - 16 * hi;   // register r holds key 32T + 16 hi + r
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t j = t * BC + 32 * T + 16 * hi + r;
-          if (j > row) sT[T][r] = -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * T + r > jrel) sT[T][r] = -__builtin_inff();
     }
     // block maxima of the raw scores; lanes l and l+32 hold the two halves of each block
-    float mx0 = sT[0][0], mx1 = sT[1][0];
+    float a0 = fmaxf(fmaxf(sT[0][0], sT[0][1]), sT[0][2]);
+    float a1 = fmaxf(fmaxf(sT[1][0], sT[1][1]), sT[1][2]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      mx0 = fmaxf(mx0, sT[0][r]);
-      mx1 = fmaxf(mx1, sT[1][r]);
+    for (int r = 3; r < 15; r += 2) {
+      a0 = fmaxf(fmaxf(a0, sT[0][r]), sT[0][r + 1]);
+      a1 = fmaxf(fmaxf(a1, sT[1][r]), sT[1][r + 1]);
     }
+    const float mx0 = fmaxf(a0, sT[0][15]), mx1 = fmaxf(a1, sT[1][15]);
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
     const float bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
     const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    q.alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
     m_run = m_new;
     // E8M0 scale of each P block from its max p = exp2((bmax - m) c); the row's own maximum gives
     // exactly exp2(0) = 1.  Exponents below -126 are clamped (affects only P < 2^-124).
     const float pm0 = __builtin_amdgcn_exp2f((bmax0 - m_new) * c);
     const float pm1 = __builtin_amdgcn_exp2f((bmax1 - m_new) * c);
-    const int sb0 = max((int)(__float_as_uint(pm0) >> 23) - 2, 1);
-    const int sb1 = max((int)(__float_as_uint(pm1) >> 23) - 2, 1);
-    const float sc0 = __uint_as_float((uint32_t)sb0 << 23);
-    const float sc1 = __uint_as_float((uint32_t)sb1 << 23);
-    // p = exp2(s c - m c) and E2M1 conversion against the block scale
-    const float mc = m_new * c;
+    q.sb0 = max((int)(__float_as_uint(pm0) >> 23) - 2, 1);
+    q.sb1 = max((int)(__float_as_uint(pm1) >> 23) - 2, 1);
+    q.sc0 = __uint_as_float((uint32_t)q.sb0 << 23);
+    q.sc1 = __uint_as_float((uint32_t)q.sb1 << 23);
+    q.mc = m_new * c;
+  };
+  // ---- phase 2: p = exp2(s c - m c), E2M1 codes, regroup, history rescale, l and PV ----
+  auto softmax_pv = [&](v16f* sT, const Soft& q, const VOps& v) {
     uint32_t pk[2][2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const float sc = T == 0 ? sc0 : sc1;
+      const float sc = T == 0 ? q.sc0 : q.sc1;
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -q.mc));
         uint32_t u = 0;
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
@@ -301,31 +328,28 @@ fwd_kernel(FwdParams p) {
     auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
     auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
     const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
-    const int psc = hi ? sb1 : sb0;
+    const int psc = hi ? q.sb1 : q.sb0;
 
     // history rescale (skipped when no row of the wave raised its max)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(q.alpha != 1.0f) != 0) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
-      auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
-      lsum[0] *= alpha;
+        for (int r = 0; r < 16; ++r) o[ct][r] *= q.alpha;
+      auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(q.alpha), __float_as_uint(q.alpha), false, false);
+      lsum[0] *= q.alpha;
       lsum[1] *= __uint_as_float(ah[1]);
     }
     // l += sum P~ (matrix core) and acc += P~ V^
     lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(ones_a), pb, lsum, 4, 4, 0, 127, 0, psc);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const v4i va = *reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32);
-      const int vsc = base[vsr_off + ct * 64];
-      o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(va), pb, o[ct], 4, 4, 0, vsc, 0, psc);
-    }
+    for (int ct = 0; ct < CT; ++ct)
+      o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(v.a[ct]), pb, o[ct], 4, 4, 0, v.s[ct], 0, psc);
   };
 
   // ---- tile loop ----
-  const int64_t ntiles = CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC);
-  auto active = [&](int64_t t) { return !CAUSAL || (t * BC <= qw + 31); };
+  const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC));
+  const int last_active = CAUSAL ? (int)((qw + 31) / BC) : ntiles - 1;   // wave-uniform
 
   load_tile(0);
   store_tile(0);
@@ -336,13 +360,25 @@ fwd_kernel(FwdParams p) {
   __syncthreads();
 
   v16f sA[2], sB[2];
-  if (active(0)) compute_s(0, sA);
+  {
+    KOps k0;
+    read_k(0, k0);
+    mfma_s(k0, sA);
+  }
   int st_cur = 0, st_next = 1, st_pref = 2;
-  auto step = [&](int64_t t, v16f* cur, v16f* nxt) {
+  auto step = [&](int t, v16f* cur, v16f* nxt) {
     const bool pref = t + 2 < ntiles;
+    const bool do_next = t + 1 <= last_active;
+    const bool do_cur = t <= last_active;
     if (pref) load_tile(t + 2);
-    if (t + 1 < ntiles && active(t + 1)) compute_s(st_next, nxt);
-    if (active(t)) softmax_pv(t, st_cur, cur);
+    KOps kn;
+    VOps vc;
+    if (do_next) read_k(st_next, kn);
+    if (do_cur) read_v(st_cur, vc);
+    Soft q;
+    if (do_cur) softmax_max(t, cur, q);
+    if (do_next) mfma_s(kn, nxt);
+    if (do_cur) softmax_pv(cur, q, vc);
     if (pref) store_tile(st_pref);
     __syncthreads();
     const int tmp = st_cur;
@@ -350,7 +386,7 @@ fwd_kernel(FwdParams p) {
     st_next = st_pref;
     st_pref = tmp;
   };
-  for (int64_t t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < ntiles; t += 2) {
     step(t, sA, sB);
     if (t + 1 >= ntiles) break;
     step(t + 1, sB, sA);

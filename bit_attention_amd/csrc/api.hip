@@ -105,7 +105,7 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
 
 int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
   if (check_dims(B, Hq, Hkv, N, d) != ATTN_FP4_OK) return -1;
-  return attnfp4::bwd_workspace_bytes(B, Hq, N, d);
+  return attnfp4::bwd_workspace_layout(B, Hq, Hkv, N, d).total;
 }
 
 int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
@@ -117,10 +117,11 @@ int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
   if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
-  const int64_t need = attnfp4::bwd_workspace_bytes(a->B, a->Hq, a->N, a->d);
+  const attnfp4::BwdWorkspace ws = attnfp4::bwd_workspace_layout(a->B, a->Hq, a->Hkv, a->N, a->d);
   if (a->workspace == nullptr || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 ||
-      a->workspace_bytes < need)
+      a->workspace_bytes < ws.total)
     return ATTN_FP4_E_WORKSPACE;
+  if (a->B * a->Hq > 65535) return ATTN_FP4_E_INVALID_ARG;   // grid z of the transposes
   st = check_device();
   if (st != ATTN_FP4_OK) return st;
   attnfp4::BwdParams p;
@@ -137,8 +138,14 @@ int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
   p.dq = (uint16_t*)a->dq;
   p.dk = (uint16_t*)a->dk;
   p.dv = (uint16_t*)a->dv;
-  p.delta = (float*)a->workspace;
-  p.dq_acc = (float*)((uint8_t*)a->workspace + ((a->B * a->Hq * a->N * 4 + 255) / 256) * 256);
+  uint8_t* w = (uint8_t*)a->workspace;
+  p.delta = (float*)(w + ws.delta);
+  p.mq = (float*)(w + ws.mq);
+  p.il = (float*)(w + ws.il);
+  p.vb = (uint16_t*)(w + ws.vb);
+  p.kt = (uint16_t*)(w + ws.kt);
+  p.qt = (uint16_t*)(w + ws.qt);
+  p.dot = (uint16_t*)(w + ws.dot);
   p.B = a->B;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;

@@ -1,16 +1,575 @@
-// Attn-QAT backward with FP4 recomputation of the scores (gfx950).  Placeholder launch until the
-// kernels land: reports "not supported" so the C-ABI returns ATTN_FP4_E_UNSUPPORTED.
+// Attn-QAT backward with FP4 recomputation of the scores, for gfx950.
+//
+// What is computed (Attn-QAT abstract: (1) the backward recomputes the attention scores with the
+// same low-precision QK^T as the forward, (2) the D term of the FlashAttention gradient is taken
+// from the FP4 forward's own output rather than assuming O = PV in high precision).  With the
+// forward's final row max m and row sum l, and gradients passing straight through the quantizers:
+//   D_i  = sum_c dO_ic O_ic                                (fp32)
+//   S^   = Q^ K^T * scale  (scaled FP4 MFMA, as in the forward)
+//   p    = exp(S^ - m),  P = p / l,  A = MXFP4(p) / l      (P requantized per 32-key block)
+//   dV   = A^T dO,  dP = dO V^T,  dS = P o (dP - D)
+//   dQ   = scale dS K^,  dK = scale dS^T Q^               (bf16 MFMA, fp32 accumulation)
+//
+// Kernels (one launch each, all on the caller's stream):
+//  1. rows: D, m log2(e) and 1/l per query row.
+//  2. transposes: bf16 copies of the dequantized operands in the layouts the bf16 MFMAs read
+//     (V^ as [N, d]; K^, Q^ and dO as [d, N]); FP4 * 2^e is exact in bf16.
+//  3. dK/dV: a workgroup owns 64 keys (two 32-key pairs of waves) and walks all query rows of the
+//     KV head's query heads in tiles of 64.  S^T and dP^T are computed with one lane per query so
+//     that the 32-key P blocks sit in one lane pair, P~ is requantized in registers exactly as in
+//     the forward, and A = P~/l and dS are passed through LDS in [key][query] order to feed the
+//     dV^T = dO^T A and dK^T = Q^T dS products.
+//  4. dQ: a workgroup owns 32W query rows and walks the keys in tiles of 64:
+//     dQ^T = K^T dS^T with dS^T taken straight from registers.  No atomics: dQ, dK, dV are each
+//     written once, so the backward is deterministic.
 #include "common.h"
 #include "internal.h"
 
 namespace attnfp4 {
 
-int64_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
-  const int64_t delta = ((B * Hq * N * 4 + 255) / 256) * 256;
-  const int64_t dq = ((B * Hq * N * d * 4 + 255) / 256) * 256;
-  return delta + dq;
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+
+// ---------------------------------------------------------------------------------------------
+// 1. per-row constants
+// 16 lanes per row; rows = B*Hq*N is a multiple of 16.
+__global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ m,
+                                                       const float* __restrict__ l, float* __restrict__ delta,
+                                                       float* __restrict__ mq, float* __restrict__ il,
+                                                       int64_t rows, int d) {
+  const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (r >= rows) return;
+  const int per = d / 16;                       // 8 (d = 128) or 4 (d = 64) elements per lane
+  const uint16_t* orow = o + r * d + sub * per;
+  const uint16_t* grow = dout + r * d + sub * per;
+  float acc = 0.0f;
+  for (int i = 0; i < per; i += 2) {
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(orow + i);
+    const uint32_t g = *reinterpret_cast<const uint32_t*>(grow + i);
+    acc = __builtin_fmaf(bf16_lo(a), bf16_lo(g), acc);
+    acc = __builtin_fmaf(bf16_hi(a), bf16_hi(g), acc);
+  }
+  acc += __shfl_xor(acc, 1, 16);
+  acc += __shfl_xor(acc, 2, 16);
+  acc += __shfl_xor(acc, 4, 16);
+  acc += __shfl_xor(acc, 8, 16);
+  if (sub == 0) {
+    delta[r] = acc;
+    mq[r] = m[r] * kLog2e;
+    il[r] = 1.0f / l[r];
+  }
 }
 
-hipError_t launch_bwd(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+// ---------------------------------------------------------------------------------------------
+// 2. 64x64 tile transpose to bf16: src logical [batch][R][C] -> dst [batch][C][R].
+//    FP4: src = packed E2M1 codes [R][C/2] with E8M0 scales [R][C/32] (dequantized exactly);
+//    otherwise src = bf16 [R][C].
+template <bool FP4>
+__global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __restrict__ src,
+                                                            const uint8_t* __restrict__ scl,
+                                                            uint16_t* __restrict__ dst, int64_t R, int64_t C) {
+  __shared__ uint16_t tile[64][66];
+  const int tid = threadIdx.x;
+  const int64_t bz = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  {
+    const int r = tid >> 2, cq = (tid & 3) * 16;
+    const int64_t row = bz * R + r0 + r;
+    if (FP4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(src + (row * C + c0 + cq) / 2);
+      const int e = (int)scl[row * (C / 32) + (c0 + cq) / 32] - 127;
+      const uint32_t ww[2] = {w.x, w.y};
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww[q], 1.0f, 0);
+        v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww[q], 1.0f, 1);
+        v2f c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww[q], 1.0f, 2);
+        v2f dd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ww[q], 1.0f, 3);
+        const float v[8] = {a[0], a[1], b[0], b[1], c[0], c[1], dd[0], dd[1]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)   // E2M1 * 2^e is exact in fp32 and in bf16
+          tile[r][cq + 8 * q + i] = (uint16_t)(__float_as_uint(__builtin_ldexpf(v[i], e)) >> 16);
+      }
+    } else {
+      const uint4* s = reinterpret_cast<const uint4*>(src + (row * C + c0 + cq) * 2);
+      const uint4 a = s[0], b = s[1];
+      const uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tile[r][cq + 2 * i] = (uint16_t)(ww[i] & 0xFFFF);
+        tile[r][cq + 2 * i + 1] = (uint16_t)(ww[i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid >> 2, rq = (tid & 3) * 16;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (uint32_t)tile[rq + 2 * i][c] | ((uint32_t)tile[rq + 2 * i + 1][c] << 16);
+    uint4* d = reinterpret_cast<uint4*>(dst + ((bz * C + c0 + c) * R + r0 + rq));
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The P~ block scale of one 32-key block in the backward.  The block's largest p is
+// exp2(bmax c - m log2 e); for the block holding the row's maximum it is 1 in exact arithmetic
+// (m is that maximum), but the fp32 rounding of the saved m can leave it a hair below 1, which
+// would halve the scale and saturate the maximum to 0.75.  Values within a few ulps of the row
+// maximum are therefore taken as exactly the maximum.  Exponents below -126 are clamped (affects
+// only P < 2^-124).
+__device__ __forceinline__ int p_scale_byte(float tb, float mq) {
+  const float tol = fmaxf(__builtin_fabsf(mq) * 0x1p-20f, 0x1p-22f);
+  const float pm = tb > -tol ? 1.0f : __builtin_amdgcn_exp2f(tb);
+  return max((int)(__float_as_uint(pm) >> 23) - 2, 1);
+}
+
+// ---------------------------------------------------------------------------------------------
+// 3. dK / dV.  Workgroup = 4 waves; wave w: pair p = w/2 owns keys k0 + 32p + [0, 32), half = w%2
+// takes query sub-tile `half` in the elementwise phase and channel half `half` in the products.
+template <int D>
+struct DkdvLds {
+  static constexpr int QC = 0;                        // Q^ codes [64 q][D/2]
+  static constexpr int QS = QC + 64 * D / 2;          // Q^ scales [64 q] dwords
+  static constexpr int DO = QS + 64 * 4;              // dO bf16 [64 q][D], 16-B chunks ^ (q & 7)
+  static constexpr int DOT = DO + 64 * D * 2;         // dO^T bf16 [D][64 q], chunks ^ (ch & 7)
+  static constexpr int QT = DOT + D * 64 * 2;         // Q^T bf16 [D][64 q], chunks ^ (ch & 7)
+  static constexpr int ROWS = QT + D * 64 * 2;        // mq, il, D: 3 x [64] floats
+  static constexpr int PS = ROWS + 3 * 64 * 4;        // A = P~/l bf16 [64 keys][64 q], chunks ^ (key & 7)
+  static constexpr int DS = PS + 64 * 64 * 2;         // dS bf16 [64 keys][64 q]
+  static constexpr int BYTES = DS + 64 * 64 * 2;
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(BwdParams p) {
+  using L = DkdvLds<D>;
+  constexpr int KS_STEPS = D / 64;        // FP4 k-steps of S^T
+  constexpr int DS_STEPS = D / 16;        // bf16 k-steps of dP^T
+  constexpr int CH = D / 2;               // channels accumulated per wave
+  constexpr int CT = CH / 32;             // 32-channel tiles per wave
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int pair = wave >> 1, half = wave & 1;
+
+  const int64_t N = p.N;
+  const int64_t nkt = N / 64;
+  const int64_t bg = blockIdx.x / nkt;            // b * Hkv + g
+  const int64_t k0 = (blockIdx.x - bg * nkt) * 64;
+  const int64_t b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int64_t group = p.Hq / p.Hkv;
+  const int64_t kp = k0 + 32 * pair;              // the pair's first key
+  const float c = p.c;
+
+  // ---- constant operands of this wave: K^ (FP4) and V^ (bf16) rows of the pair's 32 keys, in the
+  //      row order that makes lane l hold keys kp + 16(l/32) + r in S^T / dP^T register r ----
+  const int64_t krow = kp + row_key(l32);
+  v4i ka[KS_STEPS];
+  const uint8_t* kr = p.k_codes + (bg * N + krow) * (D / 2);
+#pragma unroll
+  for (int ks = 0; ks < KS_STEPS; ++ks) ka[ks] = *reinterpret_cast<const v4i*>(kr + 16 * hi + 32 * ks);
+  const uint8_t* ksr = p.k_scales + (bg * N + krow) * (D / 32);
+  const int ksc = (D == 128) ? (int)(ksr[hi] | (ksr[2 + hi] << 16)) : (int)ksr[hi];
+  v4i va[DS_STEPS];
+  const uint16_t* vr = p.vb + (bg * N + krow) * D;
+#pragma unroll
+  for (int s = 0; s < DS_STEPS; ++s) va[s] = *reinterpret_cast<const v4i*>(vr + 16 * s + 8 * hi);
+
+  v16f dv[CT], dk[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    dv[ct] = v16f{};
+    dk[ct] = v16f{};
+  }
+
+  const int64_t j_first = CAUSAL ? k0 / 64 : 0;   // query tiles below the keys see none of them
+  for (int64_t hh = 0; hh < group; ++hh) {
+    const int64_t h = g * group + hh;
+    const int64_t bh = b * p.Hq + h;
+    for (int64_t j = j_first; j < nkt; ++j) {
+      const int64_t q0 = j * 64;
+      // ---- stage the query tile: 64 rows of Q^ codes/scales, dO, dO^T, Q^T and row constants ----
+      {
+        const uint8_t* qc = p.q_codes + (bh * N + q0) * (D / 2);
+        for (int ci = tid; ci < 64 * D / 32; ci += 256)
+          *reinterpret_cast<v4i*>(smem + L::QC + 16 * ci) = *reinterpret_cast<const v4i*>(qc + 16 * ci);
+        if (tid < 64) {
+          const uint8_t* qs = p.q_scales + (bh * N + q0 + tid) * (D / 32);
+          *reinterpret_cast<uint32_t*>(smem + L::QS + 4 * tid) =
+              (D == 128) ? *reinterpret_cast<const uint32_t*>(qs) : (uint32_t)*reinterpret_cast<const uint16_t*>(qs);
+        } else if (tid < 128) {
+          const int r = tid - 64;
+          reinterpret_cast<float*>(smem + L::ROWS)[r] = p.mq[bh * N + q0 + r];
+          reinterpret_cast<float*>(smem + L::ROWS)[64 + r] = p.il[bh * N + q0 + r];
+          reinterpret_cast<float*>(smem + L::ROWS)[128 + r] = p.delta[bh * N + q0 + r];
+        }
+        constexpr int RC = D / 8;               // 16-B chunks per dO row
+        for (int ci = tid; ci < 64 * RC; ci += 256) {
+          const int q = ci / RC, cc = ci % RC;
+          *reinterpret_cast<v4i*>(smem + L::DO + q * 2 * D + 16 * (cc ^ (q & 7))) =
+              *reinterpret_cast<const v4i*>(p.dout + (bh * N + q0 + q) * D + 8 * cc);
+        }
+        for (int ci = tid; ci < D * 8; ci += 256) {
+          const int ch = ci >> 3, cc = ci & 7;
+          const int64_t off = (bh * D + ch) * N + q0 + 8 * cc;
+          *reinterpret_cast<v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+              *reinterpret_cast<const v4i*>(p.dot + off);
+          *reinterpret_cast<v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+              *reinterpret_cast<const v4i*>(p.qt + off);
+        }
+      }
+      __syncthreads();
+
+      // ---- elementwise phase: keys kp + [0,32) x queries q0 + 32 half + [0,32) ----
+      {
+        const int ql = 32 * half + l32;                  // this lane's query within the tile
+        const int64_t qrow = q0 + ql;
+        // S^T = K^ Q^T (FP4)
+        const uint8_t* qcl = smem + L::QC + ql * (D / 2);
+        const uint32_t qsw = *reinterpret_cast<const uint32_t*>(smem + L::QS + 4 * ql);
+        const int qsc = (int)(qsw >> (8 * hi));
+        v16f st = v16f{};
+        st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi)),
+                                                            st, 4, 4, 0, ksc, 0, qsc);
+        if (KS_STEPS == 2)
+          st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              widen(ka[KS_STEPS - 1]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi + 32)), st, 4, 4, 2, ksc, 2, qsc);
+        // dP^T = V^ dO^T (bf16)
+        v16f dp = v16f{};
+#pragma unroll
+        for (int s = 0; s < DS_STEPS; ++s) {
+          const int cc = 2 * s + hi;
+          const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ (ql & 7)));
+          dp = mfma_bf16(va[s], bo, dp);
+        }
+        const float mq = reinterpret_cast<const float*>(smem + L::ROWS)[ql];
+        const float il = reinterpret_cast<const float*>(smem + L::ROWS)[64 + ql];
+        const float dd = reinterpret_cast<const float*>(smem + L::ROWS)[128 + ql];
+        // register r holds key kp + 16 hi + r
+        if (CAUSAL) {
+          const int jrel = (int)(qrow - kp) - 16 * hi;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r > jrel) st[r] = -__builtin_inff();
+        }
+        float mx = st[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const int sb = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
+        const float sc = __uint_as_float((uint32_t)sb << 23);
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -mq));
+        uint32_t aw[8], sw8[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t u = 0;
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q], pr[4 * q + 1], sc, 0);
+          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
+          const v2f a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 0);   // P~ (dequantized)
+          const v2f a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 1);
+          aw[2 * q] = pk_bf16(a0[0] * il, a0[1] * il);
+          aw[2 * q + 1] = pk_bf16(a1[0] * il, a1[1] * il);
+          float ds[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[i] = pr[4 * q + i] * il * (dp[4 * q + i] - dd);
+          sw8[2 * q] = pk_bf16(ds[0], ds[1]);
+          sw8[2 * q + 1] = pk_bf16(ds[2], ds[3]);
+        }
+        // [key][query] scratch: key row 32 pair + 16 hi + r, query column ql
+        uint16_t* ps = reinterpret_cast<uint16_t*>(smem + L::PS);
+        uint16_t* dsp = reinterpret_cast<uint16_t*>(smem + L::DS);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * pair + 16 * hi + r;
+          const int col = 8 * ((ql >> 3) ^ (key & 7)) + (ql & 7);
+          const uint32_t a = aw[r >> 1], s2 = sw8[r >> 1];
+          ps[key * 64 + col] = (uint16_t)((r & 1) ? (a >> 16) : (a & 0xFFFF));
+          dsp[key * 64 + col] = (uint16_t)((r & 1) ? (s2 >> 16) : (s2 & 0xFFFF));
+        }
+      }
+      __syncthreads();
+
+      // ---- products: dV^T += dO^T A, dK^T += Q^T dS over the tile's 64 queries ----
+      {
+        const int key = 32 * pair + l32;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int cc = 2 * s + hi;                    // queries 16 s + 8 hi + [0, 8)
+          const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ (key & 7)));
+          const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ (key & 7)));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int ch = CH * half + 32 * ct + l32;
+            const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ (ch & 7)));
+            const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ (ch & 7)));
+            dv[ct] = mfma_bf16(ao, bp, dv[ct]);
+            dk[ct] = mfma_bf16(aq, bs, dk[ct]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- store: lane holds key kp + l32, channels CH half + 32 ct + 8 a + 4 hi + [0,4) ----
+  const int64_t key = kp + l32;
+  uint16_t* dvr = p.dv + (bg * N + key) * D;
+  uint16_t* dkr = p.dk + (bg * N + key) * D;
+  const float sc = p.scale_nat;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = CH * half + 32 * ct + 8 * a + 4 * hi;
+      *reinterpret_cast<uint2*>(dvr + ch) =
+          make_uint2(pk_bf16(dv[ct][4 * a], dv[ct][4 * a + 1]), pk_bf16(dv[ct][4 * a + 2], dv[ct][4 * a + 3]));
+      *reinterpret_cast<uint2*>(dkr + ch) = make_uint2(pk_bf16(sc * dk[ct][4 * a], sc * dk[ct][4 * a + 1]),
+                                                       pk_bf16(sc * dk[ct][4 * a + 2], sc * dk[ct][4 * a + 3]));
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 4. dQ.  Workgroup = W waves of 32 query rows; key tiles of 64 staged in LDS.
+template <int D>
+struct DqLds {
+  static constexpr int KC = 0;                        // K^ codes [64 slots][D/2], as in the forward
+  static constexpr int KS = KC + 64 * D / 2;          // K^ scales [64 slots] dwords
+  static constexpr int VB = KS + 64 * 4;              // V^ bf16 [64 slots][D], chunks ^ (slot & 7)
+  static constexpr int KT = VB + 64 * D * 2;          // K^T bf16 [D][64 keys], chunks ^ (ch & 7)
+  static constexpr int BYTES = KT + D * 64 * 2;
+};
+
+template <int D, int W, bool CAUSAL>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(BwdParams p) {
+  using L = DqLds<D>;
+  constexpr int NT = 64 * W;
+  constexpr int KS_STEPS = D / 64;
+  constexpr int DS_STEPS = D / 16;
+  constexpr int CT = D / 32;
+  constexpr int KCH = D / 32;             // 16-B chunks per K^ code row
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int64_t N = p.N;
+  const int64_t nqt = N / (32 * W);
+  const int64_t bh = blockIdx.x / nqt;
+  int64_t qt = blockIdx.x - bh * nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int64_t b = bh / p.Hq, h = bh - b * p.Hq;
+  const int64_t g = h / (p.Hq / p.Hkv);
+  const int64_t bg = b * p.Hkv + g;
+  const int64_t q0 = qt * 32 * W;
+  const int64_t qw = q0 + 32 * wave;
+  const int64_t row = qw + l32;
+  const float c = p.c;
+
+  // the wave's Q^ (FP4 B operand of S^T) and dO (bf16 B operand of dP^T), fixed for the kernel
+  v4i qb[KS_STEPS];
+  int qsc;
+  {
+    const uint8_t* qr = p.q_codes + (bh * N + row) * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks);
+    const uint8_t* qs = p.q_scales + (bh * N + row) * (D / 32);
+    qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 16)) : (int)qs[hi];
+  }
+  v4i ob[DS_STEPS];
+  {
+    const uint16_t* orow = p.dout + (bh * N + row) * D;
+#pragma unroll
+    for (int s = 0; s < DS_STEPS; ++s) ob[s] = *reinterpret_cast<const v4i*>(orow + 16 * s + 8 * hi);
+  }
+  const float mq = p.mq[bh * N + row], il = p.il[bh * N + row], dd = p.delta[bh * N + row];
+
+  v16f acc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v16f{};
+
+  const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / 64 + 1) : (N / 64));
+  const int last_active = CAUSAL ? (int)((qw + 31) / 64) : ntiles - 1;
+  const uint8_t* kcg = p.k_codes + bg * N * (D / 2);
+  const uint8_t* ksg = p.k_scales + bg * N * (D / 32);
+  const uint16_t* vbg = p.vb + bg * N * D;
+  const uint16_t* ktg = p.kt + bg * D * N;
+
+  for (int t = 0; t < ntiles; ++t) {
+    // ---- stage key tile t ----
+    for (int ci = tid; ci < 64 * KCH; ci += NT) {
+      const int s = ci / KCH, cc = ci % KCH;
+      const int key = 32 * (s >> 5) + row_key(s & 31);
+      *reinterpret_cast<v4i*>(smem + L::KC + s * (D / 2) + 16 * (cc ^ ((s >> 1) & (KCH - 1)))) =
+          *reinterpret_cast<const v4i*>(kcg + ((int64_t)t * 64 + key) * (D / 2) + 16 * cc);
+    }
+    for (int si = tid; si < 64; si += NT) {
+      const int key = 32 * (si >> 5) + row_key(si & 31);
+      const uint8_t* src = ksg + ((int64_t)t * 64 + key) * (D / 32);
+      *reinterpret_cast<uint32_t*>(smem + L::KS + 4 * si) =
+          (D == 128) ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+    }
+    constexpr int VC = D / 8;             // 16-B chunks per V^ bf16 row
+    for (int ci = tid; ci < 64 * VC; ci += NT) {
+      const int s = ci / VC, cc = ci % VC;
+      const int key = 32 * (s >> 5) + row_key(s & 31);
+      *reinterpret_cast<v4i*>(smem + L::VB + s * 2 * D + 16 * (cc ^ (s & 7))) =
+          *reinterpret_cast<const v4i*>(vbg + ((int64_t)t * 64 + key) * D + 8 * cc);
+    }
+    for (int ci = tid; ci < D * 8; ci += NT) {
+      const int ch = ci >> 3, cc = ci & 7;
+      *reinterpret_cast<v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+          *reinterpret_cast<const v4i*>(ktg + (int64_t)ch * N + (int64_t)t * 64 + 8 * cc);
+    }
+    __syncthreads();
+
+    if (t <= last_active) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int slot = 32 * T + l32;
+        // S^T (FP4) for the 32 keys of half T
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(smem + L::KS + 4 * slot);
+        const int ksc = (int)(kw >> (8 * hi));
+        v16f st = v16f{};
+#pragma unroll
+        for (int ks = 0; ks < KS_STEPS; ++ks) {
+          const int pc = (hi + 2 * ks) ^ ((slot >> 1) & (KCH - 1));
+          const v4i ka = *reinterpret_cast<const v4i*>(smem + L::KC + slot * (D / 2) + 16 * pc);
+          if (ks == 0)
+            st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), st, 4, 4, 0, ksc, 0, qsc);
+          else
+            st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[KS_STEPS - 1]), st, 4, 4, 2, ksc,
+                                                                2, qsc);
+        }
+        // dP^T = V^ dO^T (bf16)
+        v16f dp = v16f{};
+#pragma unroll
+        for (int s = 0; s < DS_STEPS; ++s) {
+          const int cc = 2 * s + hi;
+          const v4i a = *reinterpret_cast<const v4i*>(smem + L::VB + slot * 2 * D + 16 * (cc ^ (slot & 7)));
+          dp = mfma_bf16(a, ob[s], dp);
+        }
+        // dS = P (dP - D), P = exp2(s c - m log2 e) / l; register r holds key 64t + 32T + 16hi + r
+        if (CAUSAL && ((int64_t)t * 64 + 63 > qw)) {
+          const int jrel = (int)(row - (int64_t)t * 64) - 32 * T - 16 * hi;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r > jrel) st[r] = -__builtin_inff();
+        }
+        uint32_t dsw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i], c, -mq)) * il;
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i + 1], c, -mq)) * il;
+          dsw[i] = pk_bf16(p0 * (dp[2 * i] - dd), p1 * (dp[2 * i + 1] - dd));
+        }
+        // dQ^T += K^T dS^T: k-step s2 takes keys 32T + 16 hi + 8 s2 + [0, 8) (registers 8 s2..)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const v4i bsv = v4i{(int)dsw[4 * s2], (int)dsw[4 * s2 + 1], (int)dsw[4 * s2 + 2], (int)dsw[4 * s2 + 3]};
+          const int cc = 4 * T + 2 * hi + s2;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int ch = 32 * ct + l32;
+            const v4i a = *reinterpret_cast<const v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ (ch & 7)));
+            acc[ct] = mfma_bf16(a, bsv, acc[ct]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- store dQ = scale * dQ^T: lane holds query `row`, channels 32 ct + 8 a + 4 hi + [0,4) ----
+  uint16_t* dqr = p.dq + (bh * N + row) * D;
+  const float sc = p.scale_nat;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = 32 * ct + 8 * a + 4 * hi;
+      *reinterpret_cast<uint2*>(dqr + ch) = make_uint2(pk_bf16(sc * acc[ct][4 * a], sc * acc[ct][4 * a + 1]),
+                                                       pk_bf16(sc * acc[ct][4 * a + 2], sc * acc[ct][4 * a + 3]));
+    }
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+template <int D, bool CAUSAL>
+hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((p.N / 64) * p.Hkv * p.B)), dim3(256), 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.N % 128 == 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 4, CAUSAL>), dim3((unsigned)((p.N / 128) * p.Hq * p.B)), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 2, CAUSAL>), dim3((unsigned)((p.N / 64) * p.Hq * p.B)), dim3(128), 0,
+                       stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+  BwdWorkspace w;
+  const int64_t rows = align256(B * Hq * N * 4);
+  w.delta = 0;
+  w.mq = w.delta + rows;
+  w.il = w.mq + rows;
+  w.vb = w.il + rows;
+  w.kt = w.vb + align256(B * Hkv * N * d * 2);
+  w.qt = w.kt + align256(B * Hkv * N * d * 2);
+  w.dot = w.qt + align256(B * Hq * N * d * 2);
+  w.total = w.dot + align256(B * Hq * N * d * 2);
+  return w;
+}
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  const int64_t rows = p.B * p.Hq * p.N;
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p.o, p.dout, p.m,
+                     p.l, p.delta, p.mq, p.il, rows, (int)p.d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t d = p.d, N = p.N;
+  // V^ codes [d][N/2] -> V^ bf16 [N][d]
+  hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(N / 64), (unsigned)(d / 64), (unsigned)(p.B * p.Hkv)),
+                     dim3(256), 0, stream, p.v_codes, p.v_scales, p.vb, d, N);
+  // K^ codes [N][d/2] -> K^T bf16 [d][N]; Q^ likewise; dO bf16 [N][d] -> dO^T [d][N]
+  hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hkv)),
+                     dim3(256), 0, stream, p.k_codes, p.k_scales, p.kt, N, d);
+  hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
+                     dim3(256), 0, stream, p.q_codes, p.q_scales, p.qt, N, d);
+  hipLaunchKernelGGL(bwd_transpose_kernel<false>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
+                     dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.d == 128) return p.causal ? launch_main<128, true>(p, stream) : launch_main<128, false>(p, stream);
+  return p.causal ? launch_main<64, true>(p, stream) : launch_main<64, false>(p, stream);
+}
 
 }  // namespace attnfp4

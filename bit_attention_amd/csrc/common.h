@@ -13,6 +13,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Key held by row r (0..31) of a 32x32 S^T MFMA tile: r = 8a + 4b + c -> key 16b + 4a + c.  With
+// the 32x32 MFMA output layout (register i of lane l is row 8(i/4) + 4(l/32) + i%4) this puts key
+// 16(l/32) + i in register i of lane l, i.e. each lane holds 16 consecutive keys.
+__device__ __forceinline__ int row_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  v2bf v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // E8M0 exponent of the MX block scale from the block's max magnitude (fp32 bits):
 // e = clamp(floor(log2 amax) - 2, -127, 127), with amax < 2^-126 counted as 2^-127.

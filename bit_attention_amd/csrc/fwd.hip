@@ -39,11 +39,6 @@ namespace {
 
 constexpr int BC = 64;  // key-tile width; part of the definition of P quantization
 
-// Key held by row r (0..31) of an S^T MFMA tile: r = 8a + 4b + c -> key 16b + 4a + c.  With the
-// 32x32 MFMA output layout (register i of lane l is row 8(i/4) + 4(l/32) + i%4) this puts key
-// 16(l/32) + i in register i of lane l.
-__device__ __forceinline__ int row_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
-
 template <int D>
 struct Stage {
   static constexpr int KC_BYTES = BC * D / 2;   // K^ codes of one tile, [slot][d/2]

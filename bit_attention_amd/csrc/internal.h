@@ -35,18 +35,29 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;     // workspace: D = rowsum(dO * O), [B, Hq, N]
-  float* dq_acc;    // workspace: fp32 dQ accumulator, [B, Hq, N, d]
+  // workspace (carved by the host layer, see BwdWorkspace)
+  float* delta;     // D = rowsum(dO * O), [B, Hq, N]
+  float* mq;        // m * log2(e), [B, Hq, N]
+  float* il;        // 1 / l, [B, Hq, N]
+  uint16_t* vb;     // V^ dequantized, bf16 [B, Hkv, N, d]
+  uint16_t* kt;     // K^ dequantized and transposed, bf16 [B, Hkv, d, N]
+  uint16_t* qt;     // Q^ dequantized and transposed, bf16 [B, Hq, d, N]
+  uint16_t* dot;    // dO transposed, bf16 [B, Hq, d, N]
   int64_t B, Hq, Hkv, N, d;
   int causal;
-  float c;
-  float scale_nat;
+  float c;          // softmax_scale * log2(e)
+  float scale_nat;  // softmax_scale
 };
+
+// Byte offsets of the backward's workspace regions (each 256-byte aligned).
+struct BwdWorkspace {
+  int64_t delta, mq, il, vb, kt, qt, dot, total;
+};
+BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
 
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
                            void* scales, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
-int64_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace attnfp4

@@ -43,4 +43,5 @@ from .attention import (  # noqa: F401
     softmax_attention,
     attn_fwd,
     attn_bwd,
+    attn_row_max,
 )

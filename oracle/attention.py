@@ -143,6 +143,34 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None):
     return O, M, L
 
 
+def attn_row_max(q, k, causal=False, scale=None, quant=True, chunk=1024):
+    """Final row max m_i = max over visible keys j of (q^_i . k^_j) * scale (float64).
+
+    This is the running max the forward ends with, written as its plain definition; the
+    backward's P~ is quantized against it.  Returns [B, Hq, N].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    fq = fake_quant_mx if quant else _identity
+    group = Hq // Hkv
+    out = np.empty((B, Hq, N))
+    for b in range(B):
+        for g in range(Hkv):
+            k_hat = fq(k[b, g], axis=-1)
+            for h in range(g * group, (g + 1) * group):
+                q_hat = fq(q[b, h], axis=-1)
+                for r0 in range(0, N, chunk):
+                    rr = np.arange(r0, min(N, r0 + chunk))
+                    s = (q_hat[rr] @ k_hat.T) * scale
+                    if causal:
+                        s = np.where(np.arange(N)[None, :] <= rr[:, None], s, -np.inf)
+                    out[b, h, rr] = s.max(axis=1)
+    return out
+
+
 def attn_bwd(q, k, v, o, do, m, l, causal=False, scale=None, quant=True,
              rows=None, key_blocks=None, chunk=1024):
     """Attn-QAT backward with FP4 recomputation of the scores.

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_bwd, attn_fwd, fake_quant_mx, softmax_attention
+from oracle import attn_bwd, attn_fwd, attn_row_max, fake_quant_mx, softmax_attention
 
 
 def rand(shape, seed, scale=1.0):
@@ -201,3 +201,10 @@ def test_backward_sampling_matches_full():
     assert np.allclose(part[0], full[0][:, :, rows], rtol=0, atol=1e-14)
     assert np.allclose(part[1], full[1][:, :, keys], rtol=0, atol=1e-14)
     assert np.allclose(part[2], full[2][:, :, keys], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_max_equals_forward_final_max(causal):
+    q, k, v = rand((1, 4, 192, 32), 40, 2.0), rand((1, 2, 192, 32), 41), rand((1, 2, 192, 32), 42)
+    _, m, _ = attn_fwd(q, k, v, causal=causal)
+    assert np.array_equal(attn_row_max(q, k, causal=causal, chunk=50), m)

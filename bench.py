@@ -81,12 +81,14 @@ def cpu_baseline(w, seconds_target=15.0):
     q = W.gen_head(w, "q", 0, 0)[None, None]
     k = W.gen_head(w, "k", 0, 0)[None, None]
     v = W.gen_head(w, "v", 0, 0)[None, None]
-    rows = W.sample_rows(w.N, 32)
+    # calibrate: fixed cost (quantizing K and V of the head) and the per-row cost
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=w.causal, rows=rows)
-    dt = time.perf_counter() - t0
-    # grow the sample toward ~seconds_target of CPU work
-    n = int(min(w.N, max(32, 32 * seconds_target / max(dt, 1e-3))))
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=W.sample_rows(w.N, 2))
+    fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=W.sample_rows(w.N, 256))
+    per_row = max(time.perf_counter() - t0 - fixed, 1e-3) / 256
+    n = int(min(w.N, max(256, (seconds_target - fixed) / per_row)))
     rows = W.sample_rows(w.N, n)
     t0 = time.perf_counter()
     oracle.attn_fwd(q, k, v, causal=w.causal, rows=rows)

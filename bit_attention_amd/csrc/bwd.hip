@@ -142,11 +142,11 @@ template <int D>
 struct DkdvLds {
   static constexpr int QC = 0;                        // Q^ codes [64 q][D/2]
   static constexpr int QS = QC + 64 * D / 2;          // Q^ scales [64 q] dwords
-  static constexpr int DO = QS + 64 * 4;              // dO bf16 [64 q][D], 16-B chunks ^ (q & 7)
-  static constexpr int DOT = DO + 64 * D * 2;         // dO^T bf16 [D][64 q], chunks ^ (ch & 7)
-  static constexpr int QT = DOT + D * 64 * 2;         // Q^T bf16 [D][64 q], chunks ^ (ch & 7)
+  static constexpr int DO = QS + 64 * 4;              // dO bf16 [64 q][D], swizzled chunks
+  static constexpr int DOT = DO + 64 * D * 2;         // dO^T bf16 [D][64 q], swizzled chunks
+  static constexpr int QT = DOT + D * 64 * 2;         // Q^T bf16 [D][64 q], swizzled chunks
   static constexpr int ROWS = QT + D * 64 * 2;        // mq, il, D: 3 x [64] floats
-  static constexpr int PS = ROWS + 3 * 64 * 4;        // A = P~/l bf16 [64 keys][64 q], chunks ^ (key & 7)
+  static constexpr int PS = ROWS + 3 * 64 * 4;        // A = P~/l bf16 [64 keys][64 q], swizzled chunks
   static constexpr int DS = PS + 64 * 64 * 2;         // dS bf16 [64 keys][64 q]
   static constexpr int BYTES = DS + 64 * 64 * 2;
 };
@@ -222,15 +222,15 @@ bwd_dkdv_kernel(BwdParams p) {
         constexpr int RC = D / 8;               // 16-B chunks per dO row
         for (int ci = tid; ci < 64 * RC; ci += 256) {
           const int q = ci / RC, cc = ci % RC;
-          *reinterpret_cast<v4i*>(smem + L::DO + q * 2 * D + 16 * (cc ^ (q & 7))) =
+          *reinterpret_cast<v4i*>(smem + L::DO + q * 2 * D + 16 * (cc ^ swz_big(q, RC))) =
               *reinterpret_cast<const v4i*>(p.dout + (bh * N + q0 + q) * D + 8 * cc);
         }
         for (int ci = tid; ci < D * 8; ci += 256) {
           const int ch = ci >> 3, cc = ci & 7;
           const int64_t off = (bh * D + ch) * N + q0 + 8 * cc;
-          *reinterpret_cast<v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+          *reinterpret_cast<v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
               *reinterpret_cast<const v4i*>(p.dot + off);
-          *reinterpret_cast<v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+          *reinterpret_cast<v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
               *reinterpret_cast<const v4i*>(p.qt + off);
         }
       }
@@ -255,7 +255,7 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int s = 0; s < DS_STEPS; ++s) {
           const int cc = 2 * s + hi;
-          const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ (ql & 7)));
+          const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, D / 8)));
           dp = mfma_bf16(va[s], bo, dp);
         }
         const float mq = reinterpret_cast<const float*>(smem + L::ROWS)[ql];
@@ -300,7 +300,7 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * pair + 16 * hi + r;
-          const int col = 8 * ((ql >> 3) ^ (key & 7)) + (ql & 7);
+          const int col = 8 * ((ql >> 3) ^ swz_big(key, 8)) + (ql & 7);
           const uint32_t a = aw[r >> 1], s2 = sw8[r >> 1];
           ps[key * 64 + col] = (uint16_t)((r & 1) ? (a >> 16) : (a & 0xFFFF));
           dsp[key * 64 + col] = (uint16_t)((r & 1) ? (s2 >> 16) : (s2 & 0xFFFF));
@@ -314,13 +314,13 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int cc = 2 * s + hi;                    // queries 16 s + 8 hi + [0, 8)
-          const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ (key & 7)));
-          const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ (key & 7)));
+          const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
+          const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int ch = CH * half + 32 * ct + l32;
-            const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ (ch & 7)));
-            const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ (ch & 7)));
+            const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+            const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
             dv[ct] = mfma_bf16(ao, bp, dv[ct]);
             dk[ct] = mfma_bf16(aq, bs, dk[ct]);
           }
@@ -353,8 +353,8 @@ template <int D>
 struct DqLds {
   static constexpr int KC = 0;                        // K^ codes [64 slots][D/2], as in the forward
   static constexpr int KS = KC + 64 * D / 2;          // K^ scales [64 slots] dwords
-  static constexpr int VB = KS + 64 * 4;              // V^ bf16 [64 slots][D], chunks ^ (slot & 7)
-  static constexpr int KT = VB + 64 * D * 2;          // K^T bf16 [D][64 keys], chunks ^ (ch & 7)
+  static constexpr int VB = KS + 64 * 4;              // V^ bf16 [64 slots][D], swizzled chunks
+  static constexpr int KT = VB + 64 * D * 2;          // K^T bf16 [D][64 keys], swizzled chunks
   static constexpr int BYTES = KT + D * 64 * 2;
 };
 
@@ -422,7 +422,7 @@ bwd_dq_kernel(BwdParams p) {
     for (int ci = tid; ci < 64 * KCH; ci += NT) {
       const int s = ci / KCH, cc = ci % KCH;
       const int key = 32 * (s >> 5) + row_key(s & 31);
-      *reinterpret_cast<v4i*>(smem + L::KC + s * (D / 2) + 16 * (cc ^ ((s >> 1) & (KCH - 1)))) =
+      *reinterpret_cast<v4i*>(smem + L::KC + s * (D / 2) + 16 * (cc ^ swz_small(s, KCH))) =
           *reinterpret_cast<const v4i*>(kcg + ((int64_t)t * 64 + key) * (D / 2) + 16 * cc);
     }
     for (int si = tid; si < 64; si += NT) {
@@ -435,12 +435,12 @@ bwd_dq_kernel(BwdParams p) {
     for (int ci = tid; ci < 64 * VC; ci += NT) {
       const int s = ci / VC, cc = ci % VC;
       const int key = 32 * (s >> 5) + row_key(s & 31);
-      *reinterpret_cast<v4i*>(smem + L::VB + s * 2 * D + 16 * (cc ^ (s & 7))) =
+      *reinterpret_cast<v4i*>(smem + L::VB + s * 2 * D + 16 * (cc ^ swz_big(s, VC))) =
           *reinterpret_cast<const v4i*>(vbg + ((int64_t)t * 64 + key) * D + 8 * cc);
     }
     for (int ci = tid; ci < D * 8; ci += NT) {
       const int ch = ci >> 3, cc = ci & 7;
-      *reinterpret_cast<v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ (ch & 7))) =
+      *reinterpret_cast<v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
           *reinterpret_cast<const v4i*>(ktg + (int64_t)ch * N + (int64_t)t * 64 + 8 * cc);
     }
     __syncthreads();
@@ -455,7 +455,7 @@ bwd_dq_kernel(BwdParams p) {
         v16f st = v16f{};
 #pragma unroll
         for (int ks = 0; ks < KS_STEPS; ++ks) {
-          const int pc = (hi + 2 * ks) ^ ((slot >> 1) & (KCH - 1));
+          const int pc = (hi + 2 * ks) ^ swz_small(slot, KCH);
           const v4i ka = *reinterpret_cast<const v4i*>(smem + L::KC + slot * (D / 2) + 16 * pc);
           if (ks == 0)
             st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), st, 4, 4, 0, ksc, 0, qsc);
@@ -468,7 +468,7 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int s = 0; s < DS_STEPS; ++s) {
           const int cc = 2 * s + hi;
-          const v4i a = *reinterpret_cast<const v4i*>(smem + L::VB + slot * 2 * D + 16 * (cc ^ (slot & 7)));
+          const v4i a = *reinterpret_cast<const v4i*>(smem + L::VB + slot * 2 * D + 16 * (cc ^ swz_big(slot, D / 8)));
           dp = mfma_bf16(a, ob[s], dp);
         }
         // dS = P (dP - D), P = exp2(s c - m log2 e) / l; register r holds key 64t + 32T + 16hi + r
@@ -493,7 +493,7 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int ch = 32 * ct + l32;
-            const v4i a = *reinterpret_cast<const v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ (ch & 7)));
+            const v4i a = *reinterpret_cast<const v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
             acc[ct] = mfma_bf16(a, bsv, acc[ct]);
           }
         }

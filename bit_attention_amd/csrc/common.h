@@ -20,6 +20,16 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // 16(l/32) + i in register i of lane l, i.e. each lane holds 16 consecutive keys.
 __device__ __forceinline__ int row_key(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
+// XOR swizzles of 16-byte chunks in LDS rows, chosen so that the MFMA operand reads (consecutive
+// lanes reading consecutive rows at one logical chunk, 16-byte per lane) hit distinct 16-byte bank
+// groups whether the LDS serves 8 or 16 such lanes per cycle.
+//  - rows of 64 B (4 chunks) or 32 B (2 chunks), as for the FP4 operand tiles:
+__device__ __forceinline__ int swz_small(int row, int nchunks) { return ((row >> 1) ^ (row >> 2)) & (nchunks - 1); }
+//  - rows of 256 B (16 chunks) or 128 B (8 chunks), as for the bf16 operand tiles:
+__device__ __forceinline__ int swz_big(int row, int nchunks) {
+  return nchunks == 16 ? (row & 15) : ((row ^ (row >> 3)) & 7);
+}
+
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   v2bf v = {(__bf16)lo, (__bf16)hi};

@@ -129,7 +129,7 @@ fwd_kernel(FwdParams p) {
     const int s = (ci / S::KCHUNKS) & (BC - 1), cc = ci % S::KCHUNKS;
     const int key = 32 * (s >> 5) + row_key(s & 31);
     kg_off[i] = key * (D / 2) + 16 * cc;
-    kl_off[i] = S::KC + s * (D / 2) + 16 * (cc ^ ((s >> 1) & (S::KCHUNKS - 1)));
+    kl_off[i] = S::KC + s * (D / 2) + 16 * (cc ^ swz_small(s, S::KCHUNKS));
   }
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -137,7 +137,7 @@ fwd_kernel(FwdParams p) {
     v_on[i] = ci < NVCH;
     const int ch = (ci >> 1) & (D - 1), cc = ci & 1;
     vg_off[i] = ch * (int)(N / 2) + 16 * cc;
-    vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ ((ch >> 2) & 1));
+    vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ swz_small(ch >> 1, 2));
   }
   // scale items of a tile: 64 K^ dwords (one per slot), then D V^ u16 (two blocks per channel);
   // in round r wave w stages items 64w + NT r + [0, 64), so the kind of item is uniform per wave
@@ -166,9 +166,9 @@ fwd_kernel(FwdParams p) {
   int kr_off[KS_STEPS];
 #pragma unroll
   for (int ks = 0; ks < KS_STEPS; ++ks)
-    kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ ((l32 >> 1) & (S::KCHUNKS - 1)));
+    kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ swz_small(l32, S::KCHUNKS));
   const int ksr_off = S::KS + 4 * l32;
-  const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ ((l32 >> 2) & 1));
+  const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ swz_small(l32 >> 1, 2));
   const int vsr_off = S::VS + 2 * l32 + hi;
 
   v4i kreg[KPT], vreg[VPT];

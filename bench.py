@@ -27,6 +27,20 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published 2.5 PF
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published 8 TB/s)
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 
+# Measured HBM traffic of one forward launch at the bench shape: rocprofv3 --pmc FETCH_SIZE and
+# --pmc WRITE_SIZE, each scaled by the factor the same counter shows on a plain 1 GiB device copy
+# (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source it was measured on.
+FWD_TRAFFIC = {"source_sha1": "f724dc5ca568802527e6a2b9b5225d09e3815ae8", "bytes": 1.051e9}
+
+
+def fwd_source_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    for f in ("bit_attention_amd/csrc/fwd.hip", "bit_attention_amd/csrc/common.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -139,6 +153,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fwd-only-reps", type=int, default=0,
                     help="if > 0: only run the forward kernel this many times (for profilers)")
+    ap.add_argument("--bwd-only-reps", type=int, default=0,
+                    help="if > 0: only run the QAT-workload backward this many times (for profilers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="if > 0: only run a plain device copy of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiler)")
@@ -161,6 +177,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copied %d bytes 3 times" % (src.numel() * 4))
+        return
+
+    if args.bwd_only_reps > 0:
+        args.steps = args.bwd_only_reps
+        log("backward", bench_backward(args, torch, ops, W))
         return
 
     w = W.WORKLOADS["dit_b1h24n32768d128"]
@@ -236,7 +257,8 @@ def main():
                    "step": "quantize Q,K,V (bf16->MXFP4) + fused FP4 attention forward",
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / PEAK_FP4_TFLOPS, "traffic": None,
+                     "frac": fwd_tflops / PEAK_FP4_TFLOPS,
+                     "traffic": FWD_TRAFFIC["bytes"] if fwd_source_sha1() == FWD_TRAFFIC["source_sha1"] else None,
                      "kernel": "attn_fp4 forward (fwd_kernel<128,...,false>)", "kernel_ms": fwd_ms,
                      "flops_per_launch": flops},
         "quantize": {"ms": quant_ms, "elements": 3 * B * H * N * d,

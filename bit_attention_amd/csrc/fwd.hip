@@ -11,12 +11,13 @@
 //   O = acc / l (bf16), saved m (natural-log units) and l.
 //
 // gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
-// K^/V^ tile through LDS (three stages: the tile being finished, the next tile whose S is
-// already on the matrix core, and the one arriving from memory; one barrier per tile).
+// K^/V^ tile through LDS (three stages, loaded two tiles ahead; one barrier per tile).  The
+// kernel is bound by the vector ALU (exp, E2M1 conversion, max), so it is shaped for three waves
+// per SIMD: while one wave waits on the matrix core or LDS, the others keep the VALU busy.
 //  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
 //    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 32 rows of each
-//    S^T MFMA are loaded with a permutation of the keys chosen so that, in the MFMA's output
-//    layout, lane l holds 16 *consecutive* keys of query l%32: keys 32T + 16(l/32) + r in
+//    S^T MFMA are loaded with a permutation of the keys (row_key) chosen so that, in the MFMA's
+//    output layout, lane l holds 16 *consecutive* keys of query l%32: keys 32T + 16(l/32) + r in
 //    register r of tile T (T = 0, 1 covers the 64-key tile).
 //  * Each 32-key P block is therefore split over the lane pair (l, l+32).  Two permlane32
 //    swaps give both lanes the block maxima; each lane converts its 32 values with the hardware
@@ -25,11 +26,9 @@
 //    the scaled FP4 MFMA, with the block's E8M0 scale as that lane's B scale.
 //  * O is accumulated transposed, O^T = V^T P~^T (A = V^ in its transposed [d, N] layout from
 //    LDS, B = the packed P~), so each lane's accumulators belong to one query and the history
-//    rescale needs no cross-lane traffic.
+//    rescale needs no cross-lane traffic; it is skipped when no row of the wave raised its max.
 //  * The denominator sum of P~ runs on the matrix core too: one 16x16x128 scaled MFMA with a
 //    constant 0/1 A operand reduces the same packed P~ registers to per-query row sums.
-//  * Software pipeline: the S^T MFMAs of tile t+1 are issued before the softmax VALU work of
-//    tile t, so the matrix core and the vector ALU work on different tiles of the same wave.
 #include "common.h"
 #include "internal.h"
 
@@ -41,10 +40,10 @@ constexpr int BC = 64;  // key-tile width; part of the definition of P quantizat
 
 template <int D>
 struct Stage {
-  static constexpr int KC_BYTES = BC * D / 2;   // K^ codes of one tile, [slot][d/2]
+  static constexpr int KC_BYTES = BC * D / 2;   // K^ codes, [slot][d/2], swizzled 16-B chunks
   static constexpr int KS_BYTES = BC * 4;       // K^ scales, one dword per slot (d/32 <= 4 bytes)
-  static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2]
-  static constexpr int VS_BYTES = D * 2;        // V^ scales, two blocks per channel
+  static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2], swizzled chunks
+  static constexpr int VS_BYTES = 32 * 2 * 4;   // V^ scales: dword [c][block], byte t = channel 32t + c
   static constexpr int KC = 0;
   static constexpr int KS = KC + KC_BYTES;
   static constexpr int VC = KS + KS_BYTES;
@@ -55,8 +54,14 @@ struct Stage {
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
+// three waves per SIMD for the 128-row workgroups at d = 128 (<= 168 VGPRs); the 64-row variant
+// keeps more staging registers per thread and runs at two
+template <int D, int W>
+constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
+
 template <int D, int W, bool CAUSAL>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W>(), waves_per_simd<D, W>())))
 fwd_kernel(FwdParams p) {
   using S = Stage<D>;
   constexpr int NT = 64 * W;                      // threads
@@ -66,7 +71,7 @@ fwd_kernel(FwdParams p) {
   constexpr int NVCH = D * 2;                     // V^ code chunks (16 B) per tile
   constexpr int KPT = (NKCH + NT - 1) / NT;
   constexpr int VPT = (NVCH + NT - 1) / NT;
-  constexpr int NSC = BC + D;                     // scale items per tile (K dwords, V u16)
+  constexpr int NSC = BC + D;                     // scale items per tile (K dwords, V pairs)
   constexpr int NSTAGE = 3;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
@@ -121,11 +126,9 @@ fwd_kernel(FwdParams p) {
 
   // ---- per-thread staging offsets (constant over tiles) ----
   int kg_off[KPT], kl_off[KPT], vg_off[VPT], vl_off[VPT];
-  bool k_on[KPT], v_on[VPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int ci = tid + i * NT;
-    k_on[i] = ci < NKCH;
     const int s = (ci / S::KCHUNKS) & (BC - 1), cc = ci % S::KCHUNKS;
     const int key = 32 * (s >> 5) + row_key(s & 31);
     kg_off[i] = key * (D / 2) + 16 * cc;
@@ -134,12 +137,11 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int ci = tid + i * NT;
-    v_on[i] = ci < NVCH;
     const int ch = (ci >> 1) & (D - 1), cc = ci & 1;
     vg_off[i] = ch * (int)(N / 2) + 16 * cc;
     vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ swz_small(ch >> 1, 2));
   }
-  // scale items of a tile: 64 K^ dwords (one per slot), then D V^ u16 (two blocks per channel);
+  // scale items of a tile: 64 K^ dwords (one per slot), then D V^ pairs (two blocks per channel);
   // in round r wave w stages items 64w + NT r + [0, 64), so the kind of item is uniform per wave
   static_assert(NSC % 64 == 0 && NT % 64 == 0, "scale items come in whole waves");
   constexpr int SR = (NSC + NT - 1) / NT;
@@ -157,19 +159,18 @@ fwd_kernel(FwdParams p) {
     } else {
       const int ch = (item - BC) & (D - 1);
       sg_off[r] = ch * (int)(N / 32);
-      sl_off[r] = S::VS + 2 * ch;
+      sl_off[r] = S::VS + 8 * (ch & 31) + (ch >> 5);   // byte ch/32 of dword [ch % 32][block 0]
     }
   }
 
   // ---- per-lane LDS read offsets (constant over tiles) ----
-  // K^ A operand: slot 32T + l32, logical chunk hi + 2ks
   int kr_off[KS_STEPS];
 #pragma unroll
   for (int ks = 0; ks < KS_STEPS; ++ks)
     kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ swz_small(l32, S::KCHUNKS));
   const int ksr_off = S::KS + 4 * l32;
   const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ swz_small(l32 >> 1, 2));
-  const int vsr_off = S::VS + 2 * l32 + hi;
+  const int vsr_off = S::VS + 8 * l32 + 4 * hi;
 
   v4i kreg[KPT], vreg[VPT];
   uint32_t sreg[SR];
@@ -178,10 +179,10 @@ fwd_kernel(FwdParams p) {
     const uint8_t* vt = vcg + (int64_t)t * (BC / 2);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (k_on[i]) kreg[i] = *reinterpret_cast<const v4i*>(kt + kg_off[i]);
+      if (NKCH % NT == 0 || tid + i * NT < NKCH) kreg[i] = *reinterpret_cast<const v4i*>(kt + kg_off[i]);
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (v_on[i]) vreg[i] = *reinterpret_cast<const v4i*>(vt + vg_off[i]);
+      if (NVCH % NT == 0 || tid + i * NT < NVCH) vreg[i] = *reinterpret_cast<const v4i*>(vt + vg_off[i]);
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
       if (!s_any[r]) continue;
@@ -198,58 +199,19 @@ fwd_kernel(FwdParams p) {
     uint8_t* base = smem + st * S::BYTES;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (k_on[i]) *reinterpret_cast<v4i*>(base + kl_off[i]) = kreg[i];
+      if (NKCH % NT == 0 || tid + i * NT < NKCH) *reinterpret_cast<v4i*>(base + kl_off[i]) = kreg[i];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (v_on[i]) *reinterpret_cast<v4i*>(base + vl_off[i]) = vreg[i];
+      if (NVCH % NT == 0 || tid + i * NT < NVCH) *reinterpret_cast<v4i*>(base + vl_off[i]) = vreg[i];
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
       if (!s_any[r]) continue;
-      if (s_is_k[r])
+      if (s_is_k[r]) {
         *reinterpret_cast<uint32_t*>(base + sl_off[r]) = sreg[r];
-      else
-        *reinterpret_cast<uint16_t*>(base + sl_off[r]) = (uint16_t)sreg[r];
-    }
-  };
-
-  // ---- S^T = K^ Q^T for one tile (two 32-key halves); operands are read first, MFMAs later ----
-  struct KOps {
-    v4i a[2][KS_STEPS];
-    uint32_t w[2];
-  };
-  auto read_k = [&](int st, KOps& k) {
-    const uint8_t* base = smem + st * S::BYTES;
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      // the slot's d-block scales [b0 b1 b2 b3]; lane half hi needs block 2ks + hi
-      k.w[T] = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
-#pragma unroll
-      for (int ks = 0; ks < KS_STEPS; ++ks)
-        k.a[T][ks] = *reinterpret_cast<const v4i*>(base + kr_off[ks] + T * 32 * (D / 2));
-    }
-  };
-  auto mfma_s = [&](const KOps& k, v16f* sT) {
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int ksc = (int)(k.w[T] >> (8 * hi));   // byte 0: k-step 0, byte 2: k-step 1
-      v16f acc = v16f{};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(k.a[T][0]), widen(qb[0]), acc, 4, 4, 0, ksc, 0, qsc);
-      if (KS_STEPS == 2)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(k.a[T][KS_STEPS - 1]), widen(qb[KS_STEPS - 1]),
-                                                             acc, 4, 4, 2, ksc, 2, qsc);
-      sT[T] = acc;
-    }
-  };
-  struct VOps {
-    v4i a[CT];
-    int s[CT];
-  };
-  auto read_v = [&](int st, VOps& v) {
-    const uint8_t* base = smem + st * S::BYTES;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      v.a[ct] = *reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32);
-      v.s[ct] = base[vsr_off + ct * 64];
+      } else {
+        base[sl_off[r]] = (uint8_t)sreg[r];              // block 0 of the channel
+        base[sl_off[r] + 4] = (uint8_t)(sreg[r] >> 8);   // block 1
+      }
     }
   };
 
@@ -260,13 +222,23 @@ fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   const float c = p.c;
 
-  // ---- online softmax, phase 1: mask, running max, block scales of P~ ----
-  struct Soft {
-    float mc, alpha, sc0, sc1;
-    int sb0, sb1;
-  };
-  auto softmax_max = [&](int t, v16f* sT, Soft& q) {
-    if (CAUSAL && (t * BC + BC - 1 > qw)) {       // diagonal tile: key j > row i -> -inf
+  // ---- one 64-key tile: S^T, online softmax, P~ requantization, row sums and PV ----
+  auto tile = [&](int t, const uint8_t* base) {
+    // S^T = K^ Q^T for the two 32-key halves
+    v16f sT[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
+      const int ksc = (int)(kw >> (8 * hi));     // byte 0: k-step 0, byte 2: k-step 1
+      const v4i ka0 = *reinterpret_cast<const v4i*>(base + kr_off[0] + T * 32 * (D / 2));
+      sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
+      if (KS_STEPS == 2) {
+        const v4i ka1 = *reinterpret_cast<const v4i*>(base + kr_off[KS_STEPS - 1] + T * 32 * (D / 2));
+        sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka1), widen(qb[KS_STEPS - 1]), sT[T], 4, 4, 2,
+                                                               ksc, 2, qsc);
+      }
+    }
+    if (CAUSAL && ((int64_t)t * BC + BC - 1 > qw)) {   // diagonal tile: key j > row i -> -inf
       const int jrel = (int)(row - (int64_t)t * BC) - 16 * hi;   // register r holds key 32T + 16 hi + r
 #pragma unroll
       for (int T = 0; T < 2; ++T)
@@ -288,29 +260,23 @@ fwd_kernel(FwdParams p) {
     auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
     const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
-    q.alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
     m_run = m_new;
     // E8M0 scale of each P block from its max p = exp2((bmax - m) c); the row's own maximum gives
     // exactly exp2(0) = 1.  Exponents below -126 are clamped (affects only P < 2^-124).
-    const float pm0 = __builtin_amdgcn_exp2f((bmax0 - m_new) * c);
-    const float pm1 = __builtin_amdgcn_exp2f((bmax1 - m_new) * c);
-    q.sb0 = max((int)(__float_as_uint(pm0) >> 23) - 2, 1);
-    q.sb1 = max((int)(__float_as_uint(pm1) >> 23) - 2, 1);
-    q.sc0 = __uint_as_float((uint32_t)q.sb0 << 23);
-    q.sc1 = __uint_as_float((uint32_t)q.sb1 << 23);
-    q.mc = m_new * c;
-  };
-  // ---- phase 2: p = exp2(s c - m c), E2M1 codes, regroup, history rescale, l and PV ----
-  auto softmax_pv = [&](v16f* sT, const Soft& q, const VOps& v) {
+    const int sb0 = max((int)(__float_as_uint(__builtin_amdgcn_exp2f((bmax0 - m_new) * c)) >> 23) - 2, 1);
+    const int sb1 = max((int)(__float_as_uint(__builtin_amdgcn_exp2f((bmax1 - m_new) * c)) >> 23) - 2, 1);
+    // p = exp2(s c - m c) and E2M1 conversion against the block scale
+    const float mc = m_new * c;
     uint32_t pk[2][2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const float sc = T == 0 ? q.sc0 : q.sc1;
+      const float sc = __uint_as_float((uint32_t)(T == 0 ? sb0 : sb1) << 23);
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -q.mc));
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
         uint32_t u = 0;
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
@@ -323,26 +289,32 @@ fwd_kernel(FwdParams p) {
     auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
     auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
     const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
-    const int psc = hi ? q.sb1 : q.sb0;
+    const int psc = hi ? sb1 : sb0;
 
     // history rescale (skipped when no row of the wave raised its max)
-    if (__builtin_amdgcn_ballot_w64(q.alpha != 1.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[ct][r] *= q.alpha;
-      auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(q.alpha), __float_as_uint(q.alpha), false, false);
-      lsum[0] *= q.alpha;
+        for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+      auto ah = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+      lsum[0] *= alpha;
       lsum[1] *= __uint_as_float(ah[1]);
     }
     // l += sum P~ (matrix core) and acc += P~ V^
     lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(ones_a), pb, lsum, 4, 4, 0, 127, 0, psc);
+    const int vsw = *reinterpret_cast<const int*>(base + vsr_off);   // byte ct: channel 32 ct + l32
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-      o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(v.a[ct]), pb, o[ct], 4, 4, 0, v.s[ct], 0, psc);
+    for (int ct = 0; ct < CT; ++ct) {
+      const v8i va = widen(*reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32));
+      if (ct == 0) o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[0], 4, 4, 0, vsw, 0, psc);
+      if (ct == 1) o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[1], 4, 4, 1, vsw, 0, psc);
+      if (ct == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[2], 4, 4, 2, vsw, 0, psc);
+      if (ct == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[3], 4, 4, 3, vsw, 0, psc);
+    }
   };
 
-  // ---- tile loop ----
+  // ---- tile loop: three LDS stages, tiles loaded two ahead, unrolled so stages are static ----
   const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC));
   const int last_active = CAUSAL ? (int)((qw + 31) / BC) : ntiles - 1;   // wave-uniform
 
@@ -354,37 +326,19 @@ fwd_kernel(FwdParams p) {
   }
   __syncthreads();
 
-  v16f sA[2], sB[2];
-  {
-    KOps k0;
-    read_k(0, k0);
-    mfma_s(k0, sA);
-  }
-  int st_cur = 0, st_next = 1, st_pref = 2;
-  auto step = [&](int t, v16f* cur, v16f* nxt) {
+  auto step = [&](int t, int st) {
     const bool pref = t + 2 < ntiles;
-    const bool do_next = t + 1 <= last_active;
-    const bool do_cur = t <= last_active;
     if (pref) load_tile(t + 2);
-    KOps kn;
-    VOps vc;
-    if (do_next) read_k(st_next, kn);
-    if (do_cur) read_v(st_cur, vc);
-    Soft q;
-    if (do_cur) softmax_max(t, cur, q);
-    if (do_next) mfma_s(kn, nxt);
-    if (do_cur) softmax_pv(cur, q, vc);
-    if (pref) store_tile(st_pref);
+    if (t <= last_active) tile(t, smem + st * S::BYTES);
+    if (pref) store_tile(st == 0 ? 2 : st - 1);   // stage of tile t + 2
     __syncthreads();
-    const int tmp = st_cur;
-    st_cur = st_next;
-    st_next = st_pref;
-    st_pref = tmp;
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sA, sB);
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, 0);
     if (t + 1 >= ntiles) break;
-    step(t + 1, sB, sA);
+    step(t + 1, 1);
+    if (t + 2 >= ntiles) break;
+    step(t + 2, 2);
   }
 
   // ---- epilogue: gather l per query, normalise, store O (bf16), m, l ----
@@ -399,8 +353,8 @@ fwd_kernel(FwdParams p) {
     for (int a = 0; a < 4; ++a) {
       const int ch = 32 * ct + 8 * a + 4 * hi;
       uint2 w;
-      w.x = pack_bf16x2(o[ct][4 * a + 0] * inv, o[ct][4 * a + 1] * inv);
-      w.y = pack_bf16x2(o[ct][4 * a + 2] * inv, o[ct][4 * a + 3] * inv);
+      w.x = pk_bf16(o[ct][4 * a + 0] * inv, o[ct][4 * a + 1] * inv);
+      w.y = pk_bf16(o[ct][4 * a + 2] * inv, o[ct][4 * a + 3] * inv);
       *reinterpret_cast<uint2*>(orow + ch) = w;
     }
   if (hi == 0) {

@@ -41,7 +41,7 @@ constexpr int BC = 64;  // key-tile width; part of the definition of P quantizat
 template <int D>
 struct Stage {
   static constexpr int KC_BYTES = BC * D / 2;   // K^ codes, [slot][d/2], swizzled 16-B chunks
-  static constexpr int KS_BYTES = BC * 4;       // K^ scales, one dword per slot (d/32 <= 4 bytes)
+  static constexpr int KS_BYTES = BC * 8;       // K^ scales per slot: [b0 b1 b2 b3] and [b1 b2 b3 0]
   static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2], swizzled chunks
   static constexpr int VS_BYTES = 32 * 2 * 4;   // V^ scales: dword [c][block], byte t = channel 32t + c
   static constexpr int KC = 0;
@@ -155,7 +155,7 @@ fwd_kernel(FwdParams p) {
     if (s_is_k[r]) {
       const int key = 32 * (item >> 5) + row_key(item & 31);
       sg_off[r] = key * (D / 32);
-      sl_off[r] = S::KS + 4 * item;
+      sl_off[r] = S::KS + 8 * item;
     } else {
       const int ch = (item - BC) & (D - 1);
       sg_off[r] = ch * (int)(N / 32);
@@ -168,7 +168,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < KS_STEPS; ++ks)
     kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ swz_small(l32, S::KCHUNKS));
-  const int ksr_off = S::KS + 4 * l32;
+  const int ksr_off = S::KS + 8 * l32 + 4 * hi;
   const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ swz_small(l32 >> 1, 2));
   const int vsr_off = S::VS + 8 * l32 + 4 * hi;
 
@@ -207,7 +207,8 @@ fwd_kernel(FwdParams p) {
     for (int r = 0; r < SR; ++r) {
       if (!s_any[r]) continue;
       if (s_is_k[r]) {
-        *reinterpret_cast<uint32_t*>(base + sl_off[r]) = sreg[r];
+        // lane half hi of an S^T MFMA needs d-blocks (hi, 2 + hi) in bytes 0 and 2
+        *reinterpret_cast<uint2*>(base + sl_off[r]) = make_uint2(sreg[r], sreg[r] >> 8);
       } else {
         base[sl_off[r]] = (uint8_t)sreg[r];              // block 0 of the channel
         base[sl_off[r] + 4] = (uint8_t)(sreg[r] >> 8);   // block 1
@@ -228,8 +229,7 @@ fwd_kernel(FwdParams p) {
     v16f sT[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const uint32_t kw = *reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T);
-      const int ksc = (int)(kw >> (8 * hi));     // byte 0: k-step 0, byte 2: k-step 1
+      const int ksc = *reinterpret_cast<const int*>(base + ksr_off + 256 * T);   // byte 0: k-step 0, byte 2: k-step 1
       const v4i ka0 = *reinterpret_cast<const v4i*>(base + kr_off[0] + T * 32 * (D / 2));
       sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
       if (KS_STEPS == 2) {
@@ -262,10 +262,11 @@ fwd_kernel(FwdParams p) {
     const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
     m_run = m_new;
-    // E8M0 scale of each P block from its max p = exp2((bmax - m) c); the row's own maximum gives
-    // exactly exp2(0) = 1.  Exponents below -126 are clamped (affects only P < 2^-124).
-    const int sb0 = max((int)(__float_as_uint(__builtin_amdgcn_exp2f((bmax0 - m_new) * c)) >> 23) - 2, 1);
-    const int sb1 = max((int)(__float_as_uint(__builtin_amdgcn_exp2f((bmax1 - m_new) * c)) >> 23) - 2, 1);
+    // E8M0 scale of each P block from its max p = exp2((bmax - m) c): the biased exponent of p is
+    // floor((bmax - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
+    // that - 2, clamped below at 1 (affects only P < 2^-124; a fully masked block gives -inf).
+    const int sb0 = (int)fmaxf(__builtin_floorf((bmax0 - m_new) * c), -124.0f) + 125;
+    const int sb1 = (int)fmaxf(__builtin_floorf((bmax1 - m_new) * c), -124.0f) + 125;
     // p = exp2(s c - m c) and E2M1 conversion against the block scale
     const float mc = m_new * c;
     uint32_t pk[2][2];
@@ -277,8 +278,7 @@ fwd_kernel(FwdParams p) {
         float e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sT[T][8 * hw + i], c, -mc));
-        uint32_t u = 0;
-        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[0], e[1], sc, 0);
+        uint32_t u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(e[0]), e[0], e[1], sc, 0);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[2], e[3], sc, 1);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[4], e[5], sc, 2);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[6], e[7], sc, 3);

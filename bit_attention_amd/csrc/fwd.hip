@@ -15,15 +15,15 @@
 // kernel is bound by the vector ALU (exp, E2M1 conversion, max), so it is shaped for three waves
 // per SIMD: while one wave waits on the matrix core or LDS, the others keep the VALU busy.
 //  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
-//    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 32 rows of each
-//    S^T MFMA are loaded with a permutation of the keys (row_key) chosen so that, in the MFMA's
-//    output layout, lane l holds 16 *consecutive* keys of query l%32: keys 32T + 16(l/32) + r in
-//    register r of tile T (T = 0, 1 covers the 64-key tile).
-//  * Each 32-key P block is therefore split over the lane pair (l, l+32).  Two permlane32
-//    swaps give both lanes the block maxima; each lane converts its 32 values with the hardware
-//    E2M1 conversion (v_cvt_scalef32_pk_fp4_f32); two more swaps of the packed codes leave lane l
-//    with the 32 consecutive keys of block l/32 for query l%32 -- exactly the B-operand layout of
-//    the scaled FP4 MFMA, with the block's E8M0 scale as that lane's B scale.
+//    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 64 K^ rows of a
+//    tile are staged with a permutation of the keys (slot_key) chosen so that, in the output
+//    layout of the two S^T MFMAs, lane l holds all 32 keys of P block l/32 for query l%32 (key
+//    32(l/32) + 16T + r in register r of MFMA T).
+//  * Each lane therefore finds its block maximum alone; one permlane32 swap with the partner lane
+//    gives the tile maximum.  The lane converts its 32 values with the hardware E2M1 conversion
+//    (v_cvt_scalef32_pk_fp4_f32) against its block's E8M0 scale, and the packed codes are in
+//    the B-operand layout of the scaled FP4 MFMA as they stand, with that scale as the lane's B
+//    scale.
 //  * O is accumulated transposed, O^T = V^T P~^T (A = V^ in its transposed [d, N] layout from
 //    LDS, B = the packed P~), so each lane's accumulators belong to one query and the history
 //    rescale needs no cross-lane traffic; it is skipped when no row of the wave raised its max.
@@ -53,6 +53,18 @@ struct Stage {
 };
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+
+// raw buffer resource over [base, base + bytes) (gfx9 dword 3; out-of-range loads return 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Key held by LDS slot s (0..63) of a tile.  Slots 32T..32T+31 are the A rows of S^T MFMA T; in the
+// 32x32 output layout, register r of lane l holds row 8(r/4) + 4(l/32) + r%4, and this map makes
+// that row key 32(l/32) + 16T + r: lane l then holds all 32 keys of P block l/32 for query l%32.
+__device__ __forceinline__ int slot_key(int s) {
+  return 32 * ((s >> 2) & 1) + 16 * (s >> 5) + 4 * ((s >> 3) & 3) + (s & 3);
+}
 
 // three waves per SIMD for the 128-row workgroups at d = 128 (<= 168 VGPRs); the 64-row variant
 // keeps more staging registers per thread and runs at two
@@ -98,10 +110,12 @@ fwd_kernel(FwdParams p) {
   const int64_t qw = q0 + 32 * wave;
   const int64_t row = qw + l32;
 
-  const uint8_t* kcg = p.k_codes + (b * p.Hkv + g) * N * (D / 2);
-  const uint8_t* ksg = p.k_scales + (b * p.Hkv + g) * N * (D / 32);
-  const uint8_t* vcg = p.v_codes + (b * p.Hkv + g) * D * (N / 2);
-  const uint8_t* vsg = p.v_scales + (b * p.Hkv + g) * D * (N / 32);
+  // K^ / V^ of this KV head as buffer resources: 32-bit lane offsets, the tile offset in an SGPR
+  const int64_t kvh = b * p.Hkv + g;
+  const auto kc_rs = make_rsrc(p.k_codes + kvh * N * (D / 2), N * (D / 2));
+  const auto ks_rs = make_rsrc(p.k_scales + kvh * N * (D / 32), N * (D / 32));
+  const auto vc_rs = make_rsrc(p.v_codes + kvh * D * (N / 2), D * (N / 2));
+  const auto vs_rs = make_rsrc(p.v_scales + kvh * D * (N / 32), D * (N / 32));
 
   // ---- the wave's Q^ as the B operand of S^T = K^ Q^T (fixed for the whole kernel) ----
   v4i qb[KS_STEPS];
@@ -125,27 +139,28 @@ fwd_kernel(FwdParams p) {
   }
 
   // ---- per-thread staging offsets (constant over tiles) ----
-  int kg_off[KPT], kl_off[KPT], vg_off[VPT], vl_off[VPT];
+  uint32_t kg_off[KPT], vg_off[VPT];   // global byte offsets from the tile's (uniform) base
+  int kl_off[KPT], vl_off[VPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int ci = tid + i * NT;
     const int s = (ci / S::KCHUNKS) & (BC - 1), cc = ci % S::KCHUNKS;
-    const int key = 32 * (s >> 5) + row_key(s & 31);
-    kg_off[i] = key * (D / 2) + 16 * cc;
+    kg_off[i] = slot_key(s) * (D / 2) + 16 * cc;
     kl_off[i] = S::KC + s * (D / 2) + 16 * (cc ^ swz_small(s, S::KCHUNKS));
   }
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int ci = tid + i * NT;
     const int ch = (ci >> 1) & (D - 1), cc = ci & 1;
-    vg_off[i] = ch * (int)(N / 2) + 16 * cc;
+    vg_off[i] = (uint32_t)ch * (uint32_t)(N / 2) + 16 * cc;
     vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ swz_small(ch >> 1, 2));
   }
   // scale items of a tile: 64 K^ dwords (one per slot), then D V^ pairs (two blocks per channel);
   // in round r wave w stages items 64w + NT r + [0, 64), so the kind of item is uniform per wave
   static_assert(NSC % 64 == 0 && NT % 64 == 0, "scale items come in whole waves");
   constexpr int SR = (NSC + NT - 1) / NT;
-  int sg_off[SR], sl_off[SR];
+  uint32_t sg_off[SR];
+  int sl_off[SR];
   bool s_is_k[SR], s_any[SR];
 #pragma unroll
   for (int r = 0; r < SR; ++r) {
@@ -153,12 +168,11 @@ fwd_kernel(FwdParams p) {
     s_is_k[r] = 64 * wave + NT * r < BC;          // wave-uniform
     s_any[r] = 64 * wave + NT * r < NSC;          // wave-uniform
     if (s_is_k[r]) {
-      const int key = 32 * (item >> 5) + row_key(item & 31);
-      sg_off[r] = key * (D / 32);
+      sg_off[r] = slot_key(item) * (D / 32);
       sl_off[r] = S::KS + 8 * item;
     } else {
       const int ch = (item - BC) & (D - 1);
-      sg_off[r] = ch * (int)(N / 32);
+      sg_off[r] = (uint32_t)ch * (uint32_t)(N / 32);
       sl_off[r] = S::VS + 8 * (ch & 31) + (ch >> 5);   // byte ch/32 of dword [ch % 32][block 0]
     }
   }
@@ -175,23 +189,24 @@ fwd_kernel(FwdParams p) {
   v4i kreg[KPT], vreg[VPT];
   uint32_t sreg[SR];
   auto load_tile = [&](int t) {
-    const uint8_t* kt = kcg + (int64_t)t * (BC * D / 2);
-    const uint8_t* vt = vcg + (int64_t)t * (BC / 2);
+    t = __builtin_amdgcn_readfirstlane(t);        // keep the tile offsets in SGPRs
+    const int kt = t * (BC * D / 2), vt = t * (BC / 2);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (NKCH % NT == 0 || tid + i * NT < NKCH) kreg[i] = *reinterpret_cast<const v4i*>(kt + kg_off[i]);
+      if (NKCH % NT == 0 || tid + i * NT < NKCH)
+        kreg[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(kc_rs, (int)kg_off[i], kt, 0);
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (NVCH % NT == 0 || tid + i * NT < NVCH) vreg[i] = *reinterpret_cast<const v4i*>(vt + vg_off[i]);
+      if (NVCH % NT == 0 || tid + i * NT < NVCH)
+        vreg[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vc_rs, (int)vg_off[i], vt, 0);
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
       if (!s_any[r]) continue;
       if (s_is_k[r]) {
-        const uint8_t* src = ksg + (int64_t)t * (BC * D / 32) + sg_off[r];
-        sreg[r] = (D == 128) ? *reinterpret_cast<const uint32_t*>(src)
-                             : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+        sreg[r] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(ks_rs, (int)sg_off[r], t * (BC * D / 32), 0)
+                             : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)sg_off[r], t * (BC * D / 32), 0);
       } else {
-        sreg[r] = *reinterpret_cast<const uint16_t*>(vsg + 2 * t + sg_off[r]);
+        sreg[r] = __builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)sg_off[r], 2 * t, 0);
       }
     }
   };
@@ -239,40 +254,36 @@ fwd_kernel(FwdParams p) {
       }
     }
     if (CAUSAL && ((int64_t)t * BC + BC - 1 > qw)) {   // diagonal tile: key j > row i -> -inf
-      const int jrel = (int)(row - (int64_t)t * BC) - 16 * hi;   // register r holds key 32T + 16 hi + r
+      const int jrel = (int)(row - (int64_t)t * BC) - 32 * hi;   // register r of T holds key 32 hi + 16T + r
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * T + r > jrel) sT[T][r] = -__builtin_inff();
+          if (16 * T + r > jrel) sT[T][r] = -__builtin_inff();
     }
-    // block maxima of the raw scores; lanes l and l+32 hold the two halves of each block
-    float a0 = fmaxf(fmaxf(sT[0][0], sT[0][1]), sT[0][2]);
-    float a1 = fmaxf(fmaxf(sT[1][0], sT[1][1]), sT[1][2]);
+    // the lane's own block maximum (all 32 keys of block hi), then the partner lane's by one swap
+    float a = fmaxf(fmaxf(sT[0][0], sT[0][1]), sT[0][2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-      a0 = fmaxf(fmaxf(a0, sT[0][r]), sT[0][r + 1]);
-      a1 = fmaxf(fmaxf(a1, sT[1][r]), sT[1][r + 1]);
-    }
-    const float mx0 = fmaxf(a0, sT[0][15]), mx1 = fmaxf(a1, sT[1][15]);
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
-    const float bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-    const float bmax0 = __uint_as_float(sw2[0]), bmax1 = __uint_as_float(sw2[1]);
-    const float m_new = fmaxf(m_run, fmaxf(bmax0, bmax1));
+    for (int r = 3; r < 15; r += 2) a = fmaxf(fmaxf(a, sT[0][r]), sT[0][r + 1]);
+    a = fmaxf(fmaxf(a, sT[0][15]), sT[1][0]);
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) a = fmaxf(fmaxf(a, sT[1][r]), sT[1][r + 1]);
+    const float bm = fmaxf(a, sT[1][15]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    const float m_new = fmaxf(m_run, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
     m_run = m_new;
-    // E8M0 scale of each P block from its max p = exp2((bmax - m) c): the biased exponent of p is
-    // floor((bmax - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
+    // E8M0 scale of the block from its max p = exp2((bm - m) c): the biased exponent of p is
+    // floor((bm - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
     // that - 2, clamped below at 1 (affects only P < 2^-124; a fully masked block gives -inf).
-    const int sb0 = (int)fmaxf(__builtin_floorf((bmax0 - m_new) * c), -124.0f) + 125;
-    const int sb1 = (int)fmaxf(__builtin_floorf((bmax1 - m_new) * c), -124.0f) + 125;
-    // p = exp2(s c - m c) and E2M1 conversion against the block scale
+    const int psc = (int)fmaxf(__builtin_floorf((bm - m_new) * c), -124.0f) + 125;
+    const float sc = __uint_as_float((uint32_t)psc << 23);
+    // p = exp2(s c - m c) and E2M1 conversion against the block scale; the packed codes are
+    // already the B operand of the PV MFMA (lane l: keys 32(l/32) .. +31 of query l%32)
     const float mc = m_new * c;
     uint32_t pk[2][2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const float sc = __uint_as_float((uint32_t)(T == 0 ? sb0 : sb1) << 23);
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         float e[8];
@@ -285,11 +296,7 @@ fwd_kernel(FwdParams p) {
         pk[T][hw] = u;
       }
     }
-    // regroup: lane l gets the 32 consecutive keys of block l/32
-    auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
-    auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
-    const v8i pb = v8i{(int)x0[0], (int)x1[0], (int)x0[1], (int)x1[1], 0, 0, 0, 0};
-    const int psc = hi ? sb1 : sb0;
+    const v8i pb = v8i{(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1], 0, 0, 0, 0};
 
     // history rescale (skipped when no row of the wave raised its max)
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -309,8 +316,10 @@ fwd_kernel(FwdParams p) {
       const v8i va = widen(*reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32));
       if (ct == 0) o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[0], 4, 4, 0, vsw, 0, psc);
       if (ct == 1) o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[1], 4, 4, 1, vsw, 0, psc);
-      if (ct == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[2], 4, 4, 2, vsw, 0, psc);
-      if (ct == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[3], 4, 4, 3, vsw, 0, psc);
+      if constexpr (CT > 2) {
+        if (ct == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[2], 4, 4, 2, vsw, 0, psc);
+        if (ct == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[3], 4, 4, 3, vsw, 0, psc);
+      }
     }
   };
 

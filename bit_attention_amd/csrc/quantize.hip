@@ -47,56 +47,66 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const uint4* __restr
 }
 
 // ---- axis 1 (V): blocks along the sequence, written transposed ---------------------------
-// Grid (ceil(n / 128), ceil(d / 128), bh); block of 64 lanes, lane = channel pair.  Each load
-// instruction of the wave reads one token's 256 contiguous bytes; each lane then owns 32
-// tokens x 2 channels, i.e. two complete MX blocks, and writes 16 code bytes per channel to the
-// transposed [d, n/2] layout.
-__global__ void __launch_bounds__(64) quantize_cols_kernel(const uint32_t* __restrict__ x,
-                                                           uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales,
-                                                           int64_t n, int64_t d) {
+// Grid (ceil(n / 128), ceil(d / 128), bh); 256 threads per 128-token x 128-channel tile.  The tile
+// is read with coalesced 16-byte loads into LDS ([token][channel pair], 272-byte rows), then each
+// thread takes one channel pair and one 32-token block: two complete MX blocks, written as 16
+// code bytes per channel into the transposed [d, n/2] layout.
+constexpr int QC_TOK = 128, QC_CH = 128, QC_PITCH = 68;   // dwords per LDS row (64 + 4 padding)
+__global__ void __launch_bounds__(256) quantize_cols_kernel(const uint32_t* __restrict__ x,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            int64_t n, int64_t d) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[QC_TOK * QC_PITCH];
+  const int tid = threadIdx.x;
   const int64_t bh = blockIdx.z;
-  const int64_t cp = (int64_t)blockIdx.y * 64 + threadIdx.x;   // channel pair
-  if (2 * cp >= d) return;
-  const int64_t t0 = (int64_t)blockIdx.x * 128;
-  const uint32_t* xs = x + bh * n * (d / 2) + cp;
+  const int64_t t0 = (int64_t)blockIdx.x * QC_TOK, c0 = (int64_t)blockIdx.y * QC_CH;
+  const int ntok = (int)min((int64_t)QC_TOK, n - t0);       // multiple of 32
+  const int nch = (int)min((int64_t)QC_CH, d - c0);         // multiple of 32
+  const uint32_t* xs = x + (bh * n + t0) * (d / 2) + c0 / 2;
+  for (int k = tid; k < QC_TOK * 16; k += 256) {
+    const int r = k >> 4, cc = k & 15;                      // token, 8-channel chunk
+    if (r < ntok && 8 * cc < nch)
+      *reinterpret_cast<uint4*>(&tile[r * QC_PITCH + 4 * cc]) =
+          *reinterpret_cast<const uint4*>(xs + (int64_t)r * (d / 2) + 4 * cc);
+  }
+  __syncthreads();
+  const int cp = tid & 63, tb = tid >> 6;                   // channel pair, 32-token block
+  if (2 * cp >= nch || 32 * tb >= ntok) return;
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = tile[(32 * tb + i) * QC_PITCH + cp];
+  uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    a0 = max(a0, (w[i] << 16) & 0x7FFFFFFFu);
+    a1 = max(a1, w[i] & 0x7FFF0000u);
+  }
+  const int s0 = mx_scale_byte_from_amax_bits(a0), s1 = mx_scale_byte_from_amax_bits(a1);
+  const float i0 = exp2i(127 - s0), i1 = exp2i(127 - s1);
+  uint32_t c0w[4], c1w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t* v = w + 8 * q;
+    uint32_t u = 0, t = 0;
+    u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(v[0]) * i0, bf16_lo(v[1]) * i0, 1.0f, 0);
+    u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(v[2]) * i0, bf16_lo(v[3]) * i0, 1.0f, 1);
+    u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(v[4]) * i0, bf16_lo(v[5]) * i0, 1.0f, 2);
+    u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(v[6]) * i0, bf16_lo(v[7]) * i0, 1.0f, 3);
+    t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, bf16_hi(v[0]) * i1, bf16_hi(v[1]) * i1, 1.0f, 0);
+    t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, bf16_hi(v[2]) * i1, bf16_hi(v[3]) * i1, 1.0f, 1);
+    t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, bf16_hi(v[4]) * i1, bf16_hi(v[5]) * i1, 1.0f, 2);
+    t = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(t, bf16_hi(v[6]) * i1, bf16_hi(v[7]) * i1, 1.0f, 3);
+    c0w[q] = u;
+    c1w[q] = t;
+  }
+  const int64_t ch0 = c0 + 2 * cp, ch1 = ch0 + 1;
+  const int64_t tok = t0 + 32 * tb;
   uint8_t* cbase = codes + bh * d * (n / 2);
   uint8_t* sbase = scales + bh * d * (n / 32);
-  for (int blk = 0; blk < 4; ++blk) {
-    const int64_t tb = t0 + 32 * blk;
-    if (tb >= n) break;
-    uint32_t w[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = xs[(tb + i) * (d / 2)];
-    uint32_t a0 = 0, a1 = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      a0 = max(a0, (w[i] << 16) & 0x7FFFFFFFu);
-      a1 = max(a1, w[i] & 0x7FFF0000u);
-    }
-    const int s0 = mx_scale_byte_from_amax_bits(a0), s1 = mx_scale_byte_from_amax_bits(a1);
-    const float i0 = exp2i(127 - s0), i1 = exp2i(127 - s1);
-    uint32_t c0[4], c1[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t u = 0, v = 0;
-      u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(w[8 * q + 0]) * i0, bf16_lo(w[8 * q + 1]) * i0, 1.0f, 0);
-      u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(w[8 * q + 2]) * i0, bf16_lo(w[8 * q + 3]) * i0, 1.0f, 1);
-      u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(w[8 * q + 4]) * i0, bf16_lo(w[8 * q + 5]) * i0, 1.0f, 2);
-      u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, bf16_lo(w[8 * q + 6]) * i0, bf16_lo(w[8 * q + 7]) * i0, 1.0f, 3);
-      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, bf16_hi(w[8 * q + 0]) * i1, bf16_hi(w[8 * q + 1]) * i1, 1.0f, 0);
-      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, bf16_hi(w[8 * q + 2]) * i1, bf16_hi(w[8 * q + 3]) * i1, 1.0f, 1);
-      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, bf16_hi(w[8 * q + 4]) * i1, bf16_hi(w[8 * q + 5]) * i1, 1.0f, 2);
-      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, bf16_hi(w[8 * q + 6]) * i1, bf16_hi(w[8 * q + 7]) * i1, 1.0f, 3);
-      c0[q] = u;
-      c1[q] = v;
-    }
-    const int64_t ch0 = 2 * cp, ch1 = 2 * cp + 1;
-    *reinterpret_cast<uint4*>(cbase + ch0 * (n / 2) + tb / 2) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-    *reinterpret_cast<uint4*>(cbase + ch1 * (n / 2) + tb / 2) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-    sbase[ch0 * (n / 32) + tb / 32] = (uint8_t)s0;
-    sbase[ch1 * (n / 32) + tb / 32] = (uint8_t)s1;
-  }
+  *reinterpret_cast<uint4*>(cbase + ch0 * (n / 2) + tok / 2) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
+  *reinterpret_cast<uint4*>(cbase + ch1 * (n / 2) + tok / 2) = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
+  sbase[ch0 * (n / 32) + tok / 32] = (uint8_t)s0;
+  sbase[ch1 * (n / 32) + tok / 32] = (uint8_t)s1;
 }
 
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
@@ -108,8 +118,8 @@ hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int 
     hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint4*)x, (uint32_t*)codes, (uint8_t*)scales, n8);
   } else {
-    dim3 grid((unsigned)((n + 127) / 128), (unsigned)((d + 127) / 128), (unsigned)bh);
-    hipLaunchKernelGGL(quantize_cols_kernel, grid, dim3(64), 0, stream, (const uint32_t*)x,
+    dim3 grid((unsigned)((n + QC_TOK - 1) / QC_TOK), (unsigned)((d + QC_CH - 1) / QC_CH), (unsigned)bh);
+    hipLaunchKernelGGL(quantize_cols_kernel, grid, dim3(256), 0, stream, (const uint32_t*)x,
                        (uint8_t*)codes, (uint8_t*)scales, n, d);
   }
   return hipGetLastError();

@@ -1,7 +1,7 @@
 """Benchmark of the MXFP4 attention hot path on one MI355X.
 
 A step is one pass of the forward hot path over one batch: MXFP4 quantization of Q, K (along d)
-and V (along the sequence, transposed) followed by the fused FP4 attention forward, on the
+and V (along the sequence, block-major) followed by the fused FP4 attention forward, on the
 video-DiT-shaped workload B=1, H=24, N=32768, d=128, non-causal.  Inputs (bf16) are resident in
 HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
 
@@ -195,8 +195,8 @@ def main():
     qc = torch.empty((B, H, N, d // 2), dtype=torch.uint8, device="cuda")
     qs = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device="cuda")
     kc, ks = torch.empty_like(qc), torch.empty_like(qs)
-    vc = torch.empty((B, H, d, N // 2), dtype=torch.uint8, device="cuda")
-    vs = torch.empty((B, H, d, N // 32), dtype=torch.uint8, device="cuda")
+    vc = torch.empty((B, H, N // 32, d, 16), dtype=torch.uint8, device="cuda")
+    vs = torch.empty((B, H, N // 32, d), dtype=torch.uint8, device="cuda")
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
     m = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     l = torch.empty((B, H, N), dtype=torch.float32, device="cuda")

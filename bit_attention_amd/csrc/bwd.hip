@@ -71,9 +71,10 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------------------------------------
 // 2. 64x64 tile transpose to bf16: src logical [batch][R][C] -> dst [batch][C][R].
-//    FP4: src = packed E2M1 codes [R][C/2] with E8M0 scales [R][C/32] (dequantized exactly);
+//    FP4: src = packed E2M1 codes with E8M0 scales along C (dequantized exactly), row-major
+//    ([R][C/2] and [R][C/32]) or, with BLOCK_MAJOR, the V^ layout ([C/32][R][16], [C/32][R]);
 //    otherwise src = bf16 [R][C].
-template <bool FP4>
+template <bool FP4, bool BLOCK_MAJOR = false>
 __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __restrict__ src,
                                                             const uint8_t* __restrict__ scl,
                                                             uint16_t* __restrict__ dst, int64_t R, int64_t C) {
@@ -85,8 +86,11 @@ __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __res
     const int r = tid >> 2, cq = (tid & 3) * 16;
     const int64_t row = bz * R + r0 + r;
     if (FP4) {
-      const uint2 w = *reinterpret_cast<const uint2*>(src + (row * C + c0 + cq) / 2);
-      const int e = (int)scl[row * (C / 32) + (c0 + cq) / 32] - 127;
+      const int64_t blk = (c0 + cq) / 32;   // block-major: [batch][C/32][R][16 bytes]
+      const uint2 w = BLOCK_MAJOR
+                          ? *reinterpret_cast<const uint2*>(src + bz * (R * C / 2) + (blk * R + r0 + r) * 16 + ((cq & 31) >> 1))
+                          : *reinterpret_cast<const uint2*>(src + (row * C + c0 + cq) / 2);
+      const int e = (int)(BLOCK_MAJOR ? scl[bz * (R * C / 32) + blk * R + r0 + r] : scl[row * (C / 32) + blk]) - 127;
       const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -556,8 +560,8 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t d = p.d, N = p.N;
-  // V^ codes [d][N/2] -> V^ bf16 [N][d]
-  hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(N / 64), (unsigned)(d / 64), (unsigned)(p.B * p.Hkv)),
+  // V^ codes (block-major [N/32][d][16]) -> V^ bf16 [N][d]
+  hipLaunchKernelGGL((bwd_transpose_kernel<true, true>), dim3((unsigned)(N / 64), (unsigned)(d / 64), (unsigned)(p.B * p.Hkv)),
                      dim3(256), 0, stream, p.v_codes, p.v_scales, p.vb, d, N);
   // K^ codes [N][d/2] -> K^T bf16 [d][N]; Q^ likewise; dO bf16 [N][d] -> dO^T [d][N]
   hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hkv)),

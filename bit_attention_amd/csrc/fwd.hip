@@ -11,7 +11,8 @@
 //   O = acc / l (bf16), saved m (natural-log units) and l.
 //
 // gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
-// K^/V^ tile through LDS (three stages, loaded two tiles ahead; one barrier per tile).  The
+// K^/V^ tile through LDS (four stages filled by direct global-to-LDS loads three tiles ahead;
+// one barrier per tile).  The
 // kernel is bound by the vector ALU (exp, E2M1 conversion, max), so it is shaped for three waves
 // per SIMD: while one wave waits on the matrix core or LDS, the others keep the VALU busy.
 //  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
@@ -24,11 +25,14 @@
 //    (v_cvt_scalef32_pk_fp4_f32) against its block's E8M0 scale, and the packed codes are in
 //    the B-operand layout of the scaled FP4 MFMA as they stand, with that scale as the lane's B
 //    scale.
-//  * O is accumulated transposed, O^T = V^T P~^T (A = V^ in its transposed [d, N] layout from
-//    LDS, B = the packed P~), so each lane's accumulators belong to one query and the history
+//  * O is accumulated transposed, O^T = V^T P~^T (A = the V^ tile as [d][64 keys] in LDS, staged
+//    from the block-major V^ layout; B = the packed P~), so each lane's accumulators belong to
+//    one query and the history
 //    rescale needs no cross-lane traffic; it is skipped when no row of the wave raised its max.
 //  * The denominator sum of P~ runs on the matrix core too: one 16x16x128 scaled MFMA with a
 //    constant 0/1 A operand reduces the same packed P~ registers to per-query row sums.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -41,9 +45,10 @@ constexpr int BC = 64;  // key-tile width; part of the definition of P quantizat
 template <int D>
 struct Stage {
   static constexpr int KC_BYTES = BC * D / 2;   // K^ codes, [slot][d/2], swizzled 16-B chunks
-  static constexpr int KS_BYTES = BC * 8;       // K^ scales per slot: [b0 b1 b2 b3] and [b1 b2 b3 0]
+  // (the LDS-DMA loads of 1 and 2 bytes write one zero-extended dword per lane)
+  static constexpr int KS_BYTES = BC * 4;       // K^ scales, [slot][4]: d/32 blocks, zero padded
   static constexpr int VC_BYTES = D * BC / 2;   // V^ codes, [d][64 keys / 2], swizzled chunks
-  static constexpr int VS_BYTES = 32 * 2 * 4;   // V^ scales: dword [c][block], byte t = channel 32t + c
+  static constexpr int VS_BYTES = 256;          // V^ scales as in memory: [2 blocks][d] (d = 64: half used)
   static constexpr int KC = 0;
   static constexpr int KS = KC + KC_BYTES;
   static constexpr int VC = KS + KS_BYTES;
@@ -79,12 +84,13 @@ fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * W;                      // threads
   constexpr int KS_STEPS = D / 64;                // MFMA k-steps over the head dim
   constexpr int CT = D / 32;                      // 32-channel output tiles
-  constexpr int NKCH = BC * S::KCHUNKS;           // K^ code chunks (16 B) per tile
-  constexpr int NVCH = D * 2;                     // V^ code chunks (16 B) per tile
-  constexpr int KPT = (NKCH + NT - 1) / NT;
-  constexpr int VPT = (NVCH + NT - 1) / NT;
-  constexpr int NSC = BC + D;                     // scale items per tile (K dwords, V pairs)
-  constexpr int NSTAGE = 3;
+#ifndef ATTNFP4_FWD_STAGES
+  constexpr int NSTAGE = 4;                       // LDS stages; tiles are loaded NSTAGE - 1 ahead
+#else
+  constexpr int NSTAGE = ATTNFP4_FWD_STAGES;
+#endif
+  constexpr int PD = NSTAGE - 1;
+  static_assert(NSTAGE >= 3 && NSTAGE <= 4, "stages");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
 
@@ -138,98 +144,82 @@ fwd_kernel(FwdParams p) {
     ones_a = v4i{v, v, v, v};
   }
 
-  // ---- per-thread staging offsets (constant over tiles) ----
-  uint32_t kg_off[KPT], vg_off[VPT];   // global byte offsets from the tile's (uniform) base
-  int kl_off[KPT], vl_off[VPT];
+  // ---- tile staging: direct global -> LDS loads (buffer_load ... lds), no registers ----
+  // A tile is a fixed list of jobs, each one 64-lane LDS-DMA instruction writing a contiguous
+  // range of the stage (lane i at +16i for 16-byte loads, at +4i for 1-4 byte loads): K^ codes in
+  // 1-KB pieces, V^ codes likewise, the K^ scales, the V^ scales.  The swizzled LDS layouts are produced by choosing
+  // each lane's global source.  Wave w issues jobs w, w + W, ...; every wave issues the same
+  // number (JPW) per tile, the last job repeated where the list runs out (an identical rewrite).
+  constexpr int KCH = S::KCHUNKS;
+  constexpr int NKJ = S::KC_BYTES / 1024, NVJ = S::VC_BYTES / 1024, NVSJ = 1;
+  constexpr int NJ = NKJ + NVJ + 1 + NVSJ;
+  constexpr int JPW = (NJ + W - 1) / W;
+  static_assert(S::KC_BYTES % 1024 == 0 && S::VC_BYTES % 1024 == 0 && S::VS_BYTES % 256 == 0, "whole jobs");
+  uint32_t job_goff[JPW];                          // lane's global byte offset within tile 0
+  int job_kind[JPW], job_dst[JPW];                 // wave-uniform
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int ci = tid + i * NT;
-    const int s = (ci / S::KCHUNKS) & (BC - 1), cc = ci % S::KCHUNKS;
-    kg_off[i] = slot_key(s) * (D / 2) + 16 * cc;
-    kl_off[i] = S::KC + s * (D / 2) + 16 * (cc ^ swz_small(s, S::KCHUNKS));
-  }
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int ci = tid + i * NT;
-    const int ch = (ci >> 1) & (D - 1), cc = ci & 1;
-    vg_off[i] = (uint32_t)ch * (uint32_t)(N / 2) + 16 * cc;
-    vl_off[i] = S::VC + ch * 32 + 16 * (cc ^ swz_small(ch >> 1, 2));
-  }
-  // scale items of a tile: 64 K^ dwords (one per slot), then D V^ pairs (two blocks per channel);
-  // in round r wave w stages items 64w + NT r + [0, 64), so the kind of item is uniform per wave
-  static_assert(NSC % 64 == 0 && NT % 64 == 0, "scale items come in whole waves");
-  constexpr int SR = (NSC + NT - 1) / NT;
-  uint32_t sg_off[SR];
-  int sl_off[SR];
-  bool s_is_k[SR], s_any[SR];
-#pragma unroll
-  for (int r = 0; r < SR; ++r) {
-    const int item = 64 * wave + lane + NT * r;
-    s_is_k[r] = 64 * wave + NT * r < BC;          // wave-uniform
-    s_any[r] = 64 * wave + NT * r < NSC;          // wave-uniform
-    if (s_is_k[r]) {
-      sg_off[r] = slot_key(item) * (D / 32);
-      sl_off[r] = S::KS + 8 * item;
-    } else {
-      const int ch = (item - BC) & (D - 1);
-      sg_off[r] = (uint32_t)ch * (uint32_t)(N / 32);
-      sl_off[r] = S::VS + 8 * (ch & 31) + (ch >> 5);   // byte ch/32 of dword [ch % 32][block 0]
+  for (int i = 0; i < JPW; ++i) {
+    const int j = min(wave + W * i, NJ - 1);
+    if (j < NKJ) {                                 // K^ codes: 16-byte chunk c of the stage
+      const int c = 64 * j + lane, sl = c / KCH, cc = (c % KCH) ^ swz_small(c / KCH, KCH);
+      job_kind[i] = 0; job_dst[i] = S::KC + 1024 * j;
+      job_goff[i] = slot_key(sl) * (D / 2) + 16 * cc;
+    } else if (j < NKJ + NVJ) {                    // V^ codes: block cc of channel ch (block-major)
+      const int c = 64 * (j - NKJ) + lane, ch = c >> 1, cc = (c & 1) ^ swz_small(ch >> 1, 2);
+      job_kind[i] = 1; job_dst[i] = S::VC + 1024 * (j - NKJ);
+      job_goff[i] = 16 * D * cc + 16 * ch;
+    } else if (j == NKJ + NVJ) {                   // K^ scales, one slot per lane
+      job_kind[i] = 2; job_dst[i] = S::KS;
+      job_goff[i] = slot_key(lane) * (D / 32);
+    } else {                                       // V^ scales: the tile's 2d bytes, 4 per lane
+      job_kind[i] = 3; job_dst[i] = S::VS;
+      job_goff[i] = 4 * lane;
     }
   }
+  // job kinds: 0 K^ codes, 1 V^ codes, 2 K^ scales, 3 V^ scales; a job slot whose kind is the
+  // same for every wave is emitted without a branch
+  auto kind_of = [](int j) constexpr { return j < NKJ ? 0 : j < NKJ + NVJ ? 1 : j == NKJ + NVJ ? 2 : 3; };
+  auto issue_kind = [&](int kind, int i, int t, uint8_t* stage) {
+    auto* dst = (__attribute__((address_space(3))) void*)(stage + job_dst[i]);
+    if (kind == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kc_rs, dst, 16, (int)job_goff[i], t * (BC * D / 2), 0, 0);
+    } else if (kind == 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vc_rs, dst, 16, (int)job_goff[i], t * (BC * D / 2), 0, 0);
+    } else if (kind == 2) {                        // d/32 bytes of K^ scales per slot
+      if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rs, dst, 4, (int)job_goff[i], t * (BC * D / 32), 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rs, dst, 2, (int)job_goff[i], t * (BC * D / 32), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rs, dst, 4, (int)job_goff[i], t * (2 * D), 0, 0);
+    }
+  };
+  auto issue_job = [&](auto ic, int t, uint8_t* stage) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < JPW) {
+      constexpr int klo = kind_of(W * i < NJ - 1 ? W * i : NJ - 1);
+      constexpr int khi = kind_of(W * i + W - 1 < NJ - 1 ? W * i + W - 1 : NJ - 1);
+      if constexpr (klo == khi) issue_kind(klo, i, t, stage);
+      else issue_kind(job_kind[i], i, t, stage);
+    }
+  };
+  auto issue_tile = [&](int t, uint8_t* stage) {
+    t = __builtin_amdgcn_readfirstlane(t);         // tile offsets live in SGPRs
+    static_assert(JPW <= 6, "job slots");
+    issue_job(std::integral_constant<int, 0>{}, t, stage);
+    issue_job(std::integral_constant<int, 1>{}, t, stage);
+    issue_job(std::integral_constant<int, 2>{}, t, stage);
+    issue_job(std::integral_constant<int, 3>{}, t, stage);
+    issue_job(std::integral_constant<int, 4>{}, t, stage);
+    issue_job(std::integral_constant<int, 5>{}, t, stage);
+  };
 
   // ---- per-lane LDS read offsets (constant over tiles) ----
   int kr_off[KS_STEPS];
 #pragma unroll
   for (int ks = 0; ks < KS_STEPS; ++ks)
     kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ swz_small(l32, S::KCHUNKS));
-  const int ksr_off = S::KS + 8 * l32 + 4 * hi;
+  const int ksr_off = S::KS + 4 * l32;             // + 128 T; the lane's blocks start at byte hi
   const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ swz_small(l32 >> 1, 2));
-  const int vsr_off = S::VS + 8 * l32 + 4 * hi;
-
-  v4i kreg[KPT], vreg[VPT];
-  uint32_t sreg[SR];
-  auto load_tile = [&](int t) {
-    t = __builtin_amdgcn_readfirstlane(t);        // keep the tile offsets in SGPRs
-    const int kt = t * (BC * D / 2), vt = t * (BC / 2);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (NKCH % NT == 0 || tid + i * NT < NKCH)
-        kreg[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(kc_rs, (int)kg_off[i], kt, 0);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (NVCH % NT == 0 || tid + i * NT < NVCH)
-        vreg[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vc_rs, (int)vg_off[i], vt, 0);
-#pragma unroll
-    for (int r = 0; r < SR; ++r) {
-      if (!s_any[r]) continue;
-      if (s_is_k[r]) {
-        sreg[r] = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b32(ks_rs, (int)sg_off[r], t * (BC * D / 32), 0)
-                             : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)sg_off[r], t * (BC * D / 32), 0);
-      } else {
-        sreg[r] = __builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)sg_off[r], 2 * t, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int st) {
-    uint8_t* base = smem + st * S::BYTES;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (NKCH % NT == 0 || tid + i * NT < NKCH) *reinterpret_cast<v4i*>(base + kl_off[i]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (NVCH % NT == 0 || tid + i * NT < NVCH) *reinterpret_cast<v4i*>(base + vl_off[i]) = vreg[i];
-#pragma unroll
-    for (int r = 0; r < SR; ++r) {
-      if (!s_any[r]) continue;
-      if (s_is_k[r]) {
-        // lane half hi of an S^T MFMA needs d-blocks (hi, 2 + hi) in bytes 0 and 2
-        *reinterpret_cast<uint2*>(base + sl_off[r]) = make_uint2(sreg[r], sreg[r] >> 8);
-      } else {
-        base[sl_off[r]] = (uint8_t)sreg[r];              // block 0 of the channel
-        base[sl_off[r] + 4] = (uint8_t)(sreg[r] >> 8);   // block 1
-      }
-    }
-  };
+  const int vsr_off = S::VS + D * hi + l32;        // + 32 ct: block hi of channel 32 ct + l32
 
   v16f o[CT];
 #pragma unroll
@@ -244,7 +234,8 @@ fwd_kernel(FwdParams p) {
     v16f sT[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const int ksc = *reinterpret_cast<const int*>(base + ksr_off + 256 * T);   // byte 0: k-step 0, byte 2: k-step 1
+      // bytes 0 and 2 after the shift: blocks hi (k-step 0) and 2 + hi (k-step 1) of the slot
+      const int ksc = (int)(*reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T) >> (8 * hi));
       const v4i ka0 = *reinterpret_cast<const v4i*>(base + kr_off[0] + T * 32 * (D / 2));
       sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
       if (KS_STEPS == 2) {
@@ -310,44 +301,49 @@ fwd_kernel(FwdParams p) {
     }
     // l += sum P~ (matrix core) and acc += P~ V^
     lsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(ones_a), pb, lsum, 4, 4, 0, 127, 0, psc);
-    const int vsw = *reinterpret_cast<const int*>(base + vsr_off);   // byte ct: channel 32 ct + l32
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const v8i va = widen(*reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32));
-      if (ct == 0) o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[0], 4, 4, 0, vsw, 0, psc);
-      if (ct == 1) o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[1], 4, 4, 1, vsw, 0, psc);
-      if constexpr (CT > 2) {
-        if (ct == 2) o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[2], 4, 4, 2, vsw, 0, psc);
-        if (ct == 3) o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[3], 4, 4, 3, vsw, 0, psc);
-      }
+      const int vsc = base[vsr_off + 32 * ct];
+      o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], 4, 4, 0, vsc, 0, psc);
     }
   };
 
-  // ---- tile loop: three LDS stages, tiles loaded two ahead, unrolled so stages are static ----
+  // ---- tile loop: unrolled over the stages so that stage offsets are static ----
   const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC));
   const int last_active = CAUSAL ? (int)((qw + 31) / BC) : ntiles - 1;   // wave-uniform
 
-  load_tile(0);
-  store_tile(0);
-  if (ntiles > 1) {
-    load_tile(1);
-    store_tile(1);
-  }
-  __syncthreads();
+  // The barrier that ends step t publishes tile t + 1: each wave first waits for its own DMAs up
+  // to that tile's (all but the JPW issued by each later step), and for its LDS reads (the stage
+  // of tile t is refilled in step t + 1).  The asm statements also keep the compiler from moving
+  // memory accesses across the barrier.
+  for (int k = 0; k < PD; ++k)
+    if (k < ntiles) issue_tile(k, smem + k * S::BYTES);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  auto step = [&](int t, int st) {
-    const bool pref = t + 2 < ntiles;
-    if (pref) load_tile(t + 2);
+  static_assert(2 * JPW <= 15, "vmcnt immediate");
+  auto step = [&](int t, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    if (t + PD < ntiles) issue_tile(t + PD, smem + ((st + PD) % NSTAGE) * S::BYTES);
     if (t <= last_active) tile(t, smem + st * S::BYTES);
-    if (pref) store_tile(st == 0 ? 2 : st - 1);   // stage of tile t + 2
-    __syncthreads();
+    const int newer = min(max(ntiles - t - 2, 0), PD - 1);   // later steps that issued DMAs
+    if (PD > 2 && newer >= 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * JPW) : "memory");
+    else if (newer >= 1)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(JPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  for (int t = 0; t < ntiles; t += 3) {
-    step(t, 0);
+  for (int t = 0; t < ntiles; t += NSTAGE) {
+    step(t, std::integral_constant<int, 0>{});
     if (t + 1 >= ntiles) break;
-    step(t + 1, 1);
+    step(t + 1, std::integral_constant<int, 1>{});
     if (t + 2 >= ntiles) break;
-    step(t + 2, 2);
+    step(t + 2, std::integral_constant<int, 2>{});
+    if constexpr (NSTAGE > 3) {
+      if (t + 3 >= ntiles) break;
+      step(t + 3, std::integral_constant<int, 3>{});
+    }
   }
 
   // ---- epilogue: gather l per query, normalise, store O (bf16), m, l ----

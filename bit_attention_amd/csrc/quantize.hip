@@ -46,11 +46,13 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const uint4* __restr
   }
 }
 
-// ---- axis 1 (V): blocks along the sequence, written transposed ---------------------------
+// ---- axis 1 (V): blocks along the sequence, written block-major --------------------------
+// Output layout [n/32][d][16 code bytes] and [n/32][d] scales: the codes of one 32-token block
+// for every channel, then the next block, so that a 64-key tile of V^ is one contiguous run.
 // Grid (ceil(n / 128), ceil(d / 128), bh); 256 threads per 128-token x 128-channel tile.  The tile
 // is read with coalesced 16-byte loads into LDS ([token][channel pair], 272-byte rows), then each
-// thread takes one channel pair and one 32-token block: two complete MX blocks, written as 16
-// code bytes per channel into the transposed [d, n/2] layout.
+// thread takes one channel pair and one 32-token block: two complete MX blocks, whose 16 code
+// bytes per channel land next to those of the neighbouring channels.
 constexpr int QC_TOK = 128, QC_CH = 128, QC_PITCH = 68;   // dwords per LDS row (64 + 4 padding)
 __global__ void __launch_bounds__(256) quantize_cols_kernel(const uint32_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
@@ -99,14 +101,12 @@ __global__ void __launch_bounds__(256) quantize_cols_kernel(const uint32_t* __re
     c0w[q] = u;
     c1w[q] = t;
   }
-  const int64_t ch0 = c0 + 2 * cp, ch1 = ch0 + 1;
-  const int64_t tok = t0 + 32 * tb;
-  uint8_t* cbase = codes + bh * d * (n / 2);
-  uint8_t* sbase = scales + bh * d * (n / 32);
-  *reinterpret_cast<uint4*>(cbase + ch0 * (n / 2) + tok / 2) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
-  *reinterpret_cast<uint4*>(cbase + ch1 * (n / 2) + tok / 2) = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
-  sbase[ch0 * (n / 32) + tok / 32] = (uint8_t)s0;
-  sbase[ch1 * (n / 32) + tok / 32] = (uint8_t)s1;
+  const int64_t ch0 = c0 + 2 * cp;
+  const int64_t blk = (t0 >> 5) + tb;               // 32-token block
+  uint8_t* cb = codes + bh * d * (n / 2) + (blk * d + ch0) * 16;
+  *reinterpret_cast<uint4*>(cb) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
+  *reinterpret_cast<uint4*>(cb + 16) = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
+  *reinterpret_cast<uint16_t*>(scales + bh * d * (n / 32) + blk * d + ch0) = (uint16_t)(s0 | (s1 << 8));
 }
 
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,

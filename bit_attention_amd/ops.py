@@ -128,7 +128,8 @@ def attn_fp4_quantize(x, axis, codes=None, scales=None, stream=None):
     """MXFP4-quantize bf16 ``x`` [..., n, d].
 
     axis=0: along d -> codes [..., n, d/2], scales [..., n, d/32] (uint8).
-    axis=1: along n, transposed -> codes [..., d, n/2], scales [..., d, n/32].
+    axis=1: along n, block-major -> codes [..., n/32, d, 16], scales [..., n/32, d]
+            (for each 32-token block, the 16 code bytes of every channel).
     """
     _dev(x, torch.bfloat16, "x")
     *lead, n, d = x.shape
@@ -136,7 +137,7 @@ def attn_fp4_quantize(x, axis, codes=None, scales=None, stream=None):
     if axis == 0:
         cshape, sshape = (*lead, n, d // 2), (*lead, n, d // 32)
     else:
-        cshape, sshape = (*lead, d, n // 2), (*lead, d, n // 32)
+        cshape, sshape = (*lead, n // 32, d, 16), (*lead, n // 32, d)
     if codes is None:
         codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -150,7 +151,7 @@ def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal
                  softmax_scale=0.0, o=None, m=None, l=None, stream=None):
     """MXFP4 attention forward on pre-quantized operands (layouts of attn_fp4_quantize).
 
-    q_codes [B, Hq, N, d/2]; k_codes [B, Hkv, N, d/2]; v_codes [B, Hkv, d, N/2].
+    q_codes [B, Hq, N, d/2]; k_codes [B, Hkv, N, d/2]; v_codes [B, Hkv, N/32, d, 16].
     Returns (o bf16 [B, Hq, N, d], m fp32 [B, Hq, N], l fp32 [B, Hq, N]).
     """
     B, Hq, N, dh = q_codes.shape
@@ -159,10 +160,10 @@ def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal
     for t, name in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
                     (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
         _dev(t, torch.uint8, name)
-    if k_codes.shape != (B, Hkv, N, dh) or v_codes.shape != (B, Hkv, d, N // 2):
+    if k_codes.shape != (B, Hkv, N, dh) or v_codes.shape != (B, Hkv, N // 32, d, 16):
         raise ValueError("inconsistent operand shapes")
     if q_scales.shape != (B, Hq, N, d // 32) or k_scales.shape != (B, Hkv, N, d // 32) \
-            or v_scales.shape != (B, Hkv, d, N // 32):
+            or v_scales.shape != (B, Hkv, N // 32, d):
         raise ValueError("inconsistent scale shapes")
     dev = q_codes.device
     if o is None:
@@ -189,6 +190,9 @@ def attn_fp4_bwd_recompute(q_codes, q_scales, k_codes, k_scales, v_codes, v_scal
     d = 2 * dh
     Hkv = k_codes.shape[1]
     dev = q_codes.device
+    if k_codes.shape != (B, Hkv, N, dh) or v_codes.shape != (B, Hkv, N // 32, d, 16) \
+            or v_scales.shape != (B, Hkv, N // 32, d):
+        raise ValueError("inconsistent operand shapes")
     _dev(o, torch.bfloat16, "o")
     _dev(do, torch.bfloat16, "do")
     _dev(m, torch.float32, "m")

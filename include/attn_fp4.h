@@ -75,9 +75,12 @@ const char* attn_fp4_status_string(int32_t status);
  *   x       bf16 [bh, n, d], device.
  *   axis 0  quantize along d (Q and K): codes [bh, n, d/2] bytes,
  *           scales [bh, n, d/32] bytes.  Requires d % 32 == 0.
- *   axis 1  quantize along n (V), written transposed so that keys are the
- *           contiguous axis: codes [bh, d, n/2], scales [bh, d, n/32].
- *           Requires n % 32 == 0 and d % 32 == 0 (d % 32 for the transpose).
+ *   axis 1  quantize along n (V), block-major: for each 32-token MX block b
+ *           the 16 code bytes of every channel, then the next block --
+ *           codes [bh, n/32, d, 16] (byte j of (b, c) holds tokens 32b+2j in
+ *           the low and 32b+2j+1 in the high nibble), scales [bh, n/32, d].
+ *           A 64-key tile of V^ is then one contiguous run of 32 d bytes.
+ *           Requires n % 32 == 0 and d % 32 == 0.
  *   bh, n, d > 0.  Output is bit-exact with the rule in the header comment.
  * Errors: ATTN_FP4_E_INVALID_ARG for null or non-16-byte-aligned pointers,
  * non-positive sizes, a length not divisible as required, axis not 0/1.
@@ -89,7 +92,7 @@ int32_t attn_fp4_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32
  * Forward arguments.  Layouts (all device, contiguous):
  *   q_codes [B, Hq, N, d/2]   q_scales [B, Hq, N, d/32]   (attn_fp4_quantize axis 0)
  *   k_codes [B, Hkv, N, d/2]  k_scales [B, Hkv, N, d/32]  (axis 0)
- *   v_codes [B, Hkv, d, N/2]  v_scales [B, Hkv, d, N/32]  (axis 1, transposed)
+ *   v_codes [B, Hkv, N/32, d, 16]  v_scales [B, Hkv, N/32, d]  (axis 1, block-major)
  *   o       bf16 [B, Hq, N, d]            (output, round-to-nearest-even)
  *   m       fp32 [B, Hq, N]  final row max of the scaled scores (natural-log
  *                            units, i.e. of s = scale * q.k)        (output)

@@ -11,13 +11,17 @@ pytestmark = pytest.mark.gpu
 
 
 def ref_quant(x, axis):
-    """Oracle codes/scales in the library's layouts (axis 1 is transposed to [.., d, n])."""
+    """Oracle codes/scales in the library's layouts: axis 1 is block-major, [.., n/32, d, 16] codes
+    (the 16 bytes of one channel's 32-token block) and [.., n/32, d] scales."""
     x = np.asarray(x, dtype=np.float64)
     if axis == 0:
         c, s = oracle.quantize_mx(x, axis=-1)
         return oracle.pack_nibbles(c, -1), s
-    c, s = oracle.quantize_mx(np.swapaxes(x, -1, -2), axis=-1)
-    return oracle.pack_nibbles(c, -1), s
+    c, s = oracle.quantize_mx(np.swapaxes(x, -1, -2), axis=-1)      # per channel, along n
+    packed = oracle.pack_nibbles(c, -1)                              # [.., d, n/2]
+    d, n2 = packed.shape[-2:]
+    blocks = packed.reshape(packed.shape[:-1] + (n2 // 16, 16))     # [.., d, n/32, 16]
+    return np.ascontiguousarray(np.swapaxes(blocks, -3, -2)), np.ascontiguousarray(np.swapaxes(s, -1, -2))
 
 
 def gpu_quant(x, axis):

@@ -22,6 +22,8 @@
 //  4. dQ: a workgroup owns 32W query rows and walks the keys in tiles of 64:
 //     dQ^T = K^T dS^T with dS^T taken straight from registers.  No atomics: dQ, dK, dV are each
 //     written once, so the backward is deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -371,7 +373,7 @@ bwd_dq_kernel(BwdParams p) {
   constexpr int DS_STEPS = D / 16;
   constexpr int CT = D / 32;
   constexpr int KCH = D / 32;             // 16-B chunks per K^ code row
-  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::BYTES];   // two stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -416,94 +418,168 @@ bwd_dq_kernel(BwdParams p) {
 
   const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / 64 + 1) : (N / 64));
   const int last_active = CAUSAL ? (int)((qw + 31) / 64) : ntiles - 1;
-  const uint8_t* kcg = p.k_codes + bg * N * (D / 2);
-  const uint8_t* ksg = p.k_scales + bg * N * (D / 32);
-  const uint16_t* vbg = p.vb + bg * N * D;
-  const uint16_t* ktg = p.kt + bg * D * N;
 
-  for (int t = 0; t < ntiles; ++t) {
-    // ---- stage key tile t ----
-    for (int ci = tid; ci < 64 * KCH; ci += NT) {
-      const int s = ci / KCH, cc = ci % KCH;
-      const int key = 32 * (s >> 5) + row_key(s & 31);
-      *reinterpret_cast<v4i*>(smem + L::KC + s * (D / 2) + 16 * (cc ^ swz_small(s, KCH))) =
-          *reinterpret_cast<const v4i*>(kcg + ((int64_t)t * 64 + key) * (D / 2) + 16 * cc);
+  // ---- key-tile staging: direct global -> LDS loads into two stages, one tile ahead ----
+  // Jobs (one 64-lane LDS-DMA instruction each): K^ codes, V^ bf16 and K^T bf16 in 1-KB pieces,
+  // then the K^ scales (one dword per slot).  The LDS layouts (slot permutation, chunk swizzles)
+  // come from each lane's global source.  Wave w issues jobs w, w + W, ...; each wave issues JPW
+  // per tile, the last job repeated where the list runs out (an identical rewrite).
+  constexpr int VC = D / 8;               // 16-B chunks per V^ bf16 row
+  constexpr int NKC = 64 * D / 2 / 1024, NVB = 64 * D * 2 / 1024, NKT = D * 64 * 2 / 1024;
+  constexpr int NJ = NKC + NVB + NKT + 1;
+  constexpr int JPW = (NJ + W - 1) / W;
+  const auto kc_rs = make_rsrc(p.k_codes + bg * N * (D / 2), N * (D / 2));
+  const auto ks_rs = make_rsrc(p.k_scales + bg * N * (D / 32), N * (D / 32));
+  const auto vb_rs = make_rsrc(p.vb + bg * N * D, N * D * 2);
+  const auto kt_rs = make_rsrc(p.kt + bg * D * N, N * D * 2);
+  auto kind_of = [](int j) constexpr { return j < NKC ? 0 : j < NKC + NVB ? 1 : j < NKC + NVB + NKT ? 2 : 3; };
+  // lane's global byte offset (within tile 0) and LDS destination of job j
+  auto job_goff_of = [&](int j) -> uint32_t {
+    if (j < NKC) {
+      const int cidx = 64 * j + lane, s = cidx / KCH, cc = (cidx % KCH) ^ swz_small(s, KCH);
+      return (32 * (s >> 5) + row_key(s & 31)) * (D / 2) + 16 * cc;
+    } else if (j < NKC + NVB) {
+      const int cidx = 64 * (j - NKC) + lane, s = cidx / VC, cc = (cidx % VC) ^ swz_big(s, VC);
+      return (32 * (s >> 5) + row_key(s & 31)) * (D * 2) + 16 * cc;
+    } else if (j < NKC + NVB + NKT) {
+      const int cidx = 64 * (j - NKC - NVB) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
+      return (uint32_t)ch * (uint32_t)(N * 2) + 16 * cc;
     }
-    for (int si = tid; si < 64; si += NT) {
-      const int key = 32 * (si >> 5) + row_key(si & 31);
-      const uint8_t* src = ksg + ((int64_t)t * 64 + key) * (D / 32);
-      *reinterpret_cast<uint32_t*>(smem + L::KS + 4 * si) =
-          (D == 128) ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+    return (32 * (lane >> 5) + row_key(lane & 31)) * (D / 32);
+  };
+  auto job_dst_of = [](int j) -> int {
+    return j < NKC ? L::KC + 1024 * j
+         : j < NKC + NVB ? L::VB + 1024 * (j - NKC)
+         : j < NKC + NVB + NKT ? L::KT + 1024 * (j - NKC - NVB) : L::KS;
+  };
+  // with few jobs per wave the lane offsets are kept in registers, else recomputed per tile
+  constexpr bool PRE = JPW <= 6;
+  uint32_t job_goff[PRE ? JPW : 1];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int i = 0; i < JPW; ++i) job_goff[i] = job_goff_of(min(wave + W * i, NJ - 1));
+  }
+  auto issue_kind = [&](int kind, int i, int t, uint8_t* stage) __attribute__((always_inline)) {
+    const int j = min(wave + W * i, NJ - 1);
+    auto* dst = (__attribute__((address_space(3))) void*)(stage + job_dst_of(j));   // LDS-DMA target
+    uint32_t goff;
+    if constexpr (PRE) goff = job_goff[PRE ? i : 0];
+    else goff = job_goff_of(j);
+    if (kind == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kc_rs, dst, 16, (int)goff, t * (64 * D / 2), 0, 0);
+    } else if (kind == 1) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vb_rs, dst, 16, (int)goff, t * (64 * D * 2), 0, 0);
+    } else if (kind == 2) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kt_rs, dst, 16, (int)goff, t * (64 * 2), 0, 0);
+    } else {                                  // d/32 scale bytes per slot, one dword per lane
+      if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rs, dst, 4, (int)goff, t * (64 * D / 32), 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rs, dst, 2, (int)goff, t * (64 * D / 32), 0, 0);
     }
-    constexpr int VC = D / 8;             // 16-B chunks per V^ bf16 row
-    for (int ci = tid; ci < 64 * VC; ci += NT) {
-      const int s = ci / VC, cc = ci % VC;
-      const int key = 32 * (s >> 5) + row_key(s & 31);
-      *reinterpret_cast<v4i*>(smem + L::VB + s * 2 * D + 16 * (cc ^ swz_big(s, VC))) =
-          *reinterpret_cast<const v4i*>(vbg + ((int64_t)t * 64 + key) * D + 8 * cc);
+  };
+  auto issue_job = [&](auto ic, int t, uint8_t* stage) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < JPW) {
+      constexpr int klo = kind_of(W * i < NJ - 1 ? W * i : NJ - 1);
+      constexpr int khi = kind_of(W * i + W - 1 < NJ - 1 ? W * i + W - 1 : NJ - 1);
+      if constexpr (klo == khi) issue_kind(klo, i, t, stage);
+      else issue_kind(kind_of(min(wave + W * i, NJ - 1)), i, t, stage);
     }
-    for (int ci = tid; ci < D * 8; ci += NT) {
-      const int ch = ci >> 3, cc = ci & 7;
-      *reinterpret_cast<v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
-          *reinterpret_cast<const v4i*>(ktg + (int64_t)ch * N + (int64_t)t * 64 + 8 * cc);
-    }
-    __syncthreads();
+  };
+  auto issue_tile = [&](int t, uint8_t* stage) __attribute__((always_inline)) {
+    t = __builtin_amdgcn_readfirstlane(t);
+    static_assert(JPW <= 20, "job slots");
+    issue_job(std::integral_constant<int, 0>{}, t, stage);
+    issue_job(std::integral_constant<int, 1>{}, t, stage);
+    issue_job(std::integral_constant<int, 2>{}, t, stage);
+    issue_job(std::integral_constant<int, 3>{}, t, stage);
+    issue_job(std::integral_constant<int, 4>{}, t, stage);
+    issue_job(std::integral_constant<int, 5>{}, t, stage);
+    issue_job(std::integral_constant<int, 6>{}, t, stage);
+    issue_job(std::integral_constant<int, 7>{}, t, stage);
+    issue_job(std::integral_constant<int, 8>{}, t, stage);
+    issue_job(std::integral_constant<int, 9>{}, t, stage);
+    issue_job(std::integral_constant<int, 10>{}, t, stage);
+    issue_job(std::integral_constant<int, 11>{}, t, stage);
+    issue_job(std::integral_constant<int, 12>{}, t, stage);
+    issue_job(std::integral_constant<int, 13>{}, t, stage);
+    issue_job(std::integral_constant<int, 14>{}, t, stage);
+    issue_job(std::integral_constant<int, 15>{}, t, stage);
+    issue_job(std::integral_constant<int, 16>{}, t, stage);
+    issue_job(std::integral_constant<int, 17>{}, t, stage);
+    issue_job(std::integral_constant<int, 18>{}, t, stage);
+    issue_job(std::integral_constant<int, 19>{}, t, stage);
+  };
 
-    if (t <= last_active) {
+  auto compute = [&](int t, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const int slot = 32 * T + l32;
-        // S^T (FP4) for the 32 keys of half T
-        const uint32_t kw = *reinterpret_cast<const uint32_t*>(smem + L::KS + 4 * slot);
-        const int ksc = (int)(kw >> (8 * hi));
-        v16f st = v16f{};
+    for (int T = 0; T < 2; ++T) {
+      const int slot = 32 * T + l32;
+      // S^T (FP4) for the 32 keys of half T
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(base + L::KS + 4 * slot);
+      const int ksc = (int)(kw >> (8 * hi));
+      v16f st = v16f{};
 #pragma unroll
-        for (int ks = 0; ks < KS_STEPS; ++ks) {
-          const int pc = (hi + 2 * ks) ^ swz_small(slot, KCH);
-          const v4i ka = *reinterpret_cast<const v4i*>(smem + L::KC + slot * (D / 2) + 16 * pc);
-          if (ks == 0)
-            st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), st, 4, 4, 0, ksc, 0, qsc);
-          else
-            st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[KS_STEPS - 1]), st, 4, 4, 2, ksc,
-                                                                2, qsc);
-        }
-        // dP^T = V^ dO^T (bf16)
-        v16f dp = v16f{};
+      for (int ks = 0; ks < KS_STEPS; ++ks) {
+        const int pc = (hi + 2 * ks) ^ swz_small(slot, KCH);
+        const v4i ka = *reinterpret_cast<const v4i*>(base + L::KC + slot * (D / 2) + 16 * pc);
+        if (ks == 0)
+          st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), st, 4, 4, 0, ksc, 0, qsc);
+        else
+          st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[KS_STEPS - 1]), st, 4, 4, 2, ksc,
+                                                              2, qsc);
+      }
+      // dP^T = V^ dO^T (bf16)
+      v16f dp = v16f{};
 #pragma unroll
-        for (int s = 0; s < DS_STEPS; ++s) {
-          const int cc = 2 * s + hi;
-          const v4i a = *reinterpret_cast<const v4i*>(smem + L::VB + slot * 2 * D + 16 * (cc ^ swz_big(slot, D / 8)));
-          dp = mfma_bf16(a, ob[s], dp);
-        }
-        // dS = P (dP - D), P = exp2(s c - m log2 e) / l; register r holds key 64t + 32T + 16hi + r
-        if (CAUSAL && ((int64_t)t * 64 + 63 > qw)) {
-          const int jrel = (int)(row - (int64_t)t * 64) - 32 * T - 16 * hi;
+      for (int s = 0; s < DS_STEPS; ++s) {
+        const int cc = 2 * s + hi;
+        const v4i a = *reinterpret_cast<const v4i*>(base + L::VB + slot * 2 * D + 16 * (cc ^ swz_big(slot, D / 8)));
+        dp = mfma_bf16(a, ob[s], dp);
+      }
+      // dS = P (dP - D), P = exp2(s c - m log2 e) / l; register r holds key 64t + 32T + 16hi + r
+      if (CAUSAL && ((int64_t)t * 64 + 63 > qw)) {
+        const int jrel = (int)(row - (int64_t)t * 64) - 32 * T - 16 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r > jrel) st[r] = -__builtin_inff();
-        }
-        uint32_t dsw[8];
+        for (int r = 0; r < 16; ++r)
+          if (r > jrel) st[r] = -__builtin_inff();
+      }
+      uint32_t dsw[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i], c, -mq)) * il;
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i + 1], c, -mq)) * il;
-          dsw[i] = pk_bf16(p0 * (dp[2 * i] - dd), p1 * (dp[2 * i + 1] - dd));
-        }
-        // dQ^T += K^T dS^T: k-step s2 takes keys 32T + 16 hi + 8 s2 + [0, 8) (registers 8 s2..)
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i], c, -mq)) * il;
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i + 1], c, -mq)) * il;
+        dsw[i] = pk_bf16(p0 * (dp[2 * i] - dd), p1 * (dp[2 * i + 1] - dd));
+      }
+      // dQ^T += K^T dS^T: k-step s2 takes keys 32T + 16 hi + 8 s2 + [0, 8) (registers 8 s2..)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const v4i bsv = v4i{(int)dsw[4 * s2], (int)dsw[4 * s2 + 1], (int)dsw[4 * s2 + 2], (int)dsw[4 * s2 + 3]};
-          const int cc = 4 * T + 2 * hi + s2;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const v4i bsv = v4i{(int)dsw[4 * s2], (int)dsw[4 * s2 + 1], (int)dsw[4 * s2 + 2], (int)dsw[4 * s2 + 3]};
+        const int cc = 4 * T + 2 * hi + s2;
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const int ch = 32 * ct + l32;
-            const v4i a = *reinterpret_cast<const v4i*>(smem + L::KT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
-            acc[ct] = mfma_bf16(a, bsv, acc[ct]);
-          }
+        for (int ct = 0; ct < CT; ++ct) {
+          const int ch = 32 * ct + l32;
+          const v4i a = *reinterpret_cast<const v4i*>(base + L::KT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+          acc[ct] = mfma_bf16(a, bsv, acc[ct]);
         }
       }
     }
-    __syncthreads();
+  };
+
+  // step t: prefetch tile t + 1 into the other stage, compute tile t; the barrier that ends the
+  // step publishes tile t + 1 (each wave first waits for its own DMAs) and frees stage t.  The
+  // asm statements also keep the compiler from moving memory accesses across the barrier.
+  issue_tile(0, smem);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  auto step = [&](int t, auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    if (t + 1 < ntiles) issue_tile(t + 1, smem + (st ^ 1) * L::BYTES);
+    if (t <= last_active) compute(t, smem + st * L::BYTES);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 >= ntiles) break;
+    step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- store dQ = scale * dQ^T: lane holds query `row`, channels 32 ct + 8 a + 4 hi + [0,4) ----
@@ -527,7 +603,10 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.N % 128 == 0) {
+  if (p.N % 256 == 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, 8, CAUSAL>), dim3((unsigned)((p.N / 256) * p.Hq * p.B)), dim3(512), 0,
+                       stream, p);
+  } else if (p.N % 128 == 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, 4, CAUSAL>), dim3((unsigned)((p.N / 128) * p.Hq * p.B)), dim3(256), 0,
                        stream, p);
   } else {

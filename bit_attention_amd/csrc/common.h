@@ -30,6 +30,11 @@ __device__ __forceinline__ int swz_big(int row, int nchunks) {
   return nchunks == 16 ? (row & 15) : ((row ^ (row >> 3)) & 7);
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 dword 3; out-of-range loads return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   v2bf v = {(__bf16)lo, (__bf16)hi};

@@ -59,11 +59,6 @@ struct Stage {
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
-// raw buffer resource over [base, base + bytes) (gfx9 dword 3; out-of-range loads return 0)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
-}
-
 // Key held by LDS slot s (0..63) of a tile.  Slots 32T..32T+31 are the A rows of S^T MFMA T; in the
 // 32x32 output layout, register r of lane l holds row 8(r/4) + 4(l/32) + r%4, and this map makes
 // that row key 32(l/32) + 16T + r: lane l then holds all 32 keys of P block l/32 for query l%32.

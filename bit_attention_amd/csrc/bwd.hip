@@ -142,29 +142,35 @@ __device__ __forceinline__ int p_scale_byte(float tb, float mq) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3. dK / dV.  Workgroup = 4 waves; wave w: pair p = w/2 owns keys k0 + 32p + [0, 32), half = w%2
+// 3. dK / dV.  Workgroup = W waves; wave w: pair p = w/2 owns keys k0 + 32p + [0, 32), half = w%2
 // takes query sub-tile `half` in the elementwise phase and channel half `half` in the products.
-template <int D>
+// The query tile's operands are staged by direct global -> LDS loads in two groups that alternate
+// with the two phases of a tile: group A (Q^ codes and scales, the row constants, dO) is read by
+// the elementwise phase and refilled for the next tile during the products; group B (dO^T, Q^T)
+// is read by the products and refilled during the next elementwise phase.
+template <int D, int W>
 struct DkdvLds {
-  static constexpr int QC = 0;                        // Q^ codes [64 q][D/2]
-  static constexpr int QS = QC + 64 * D / 2;          // Q^ scales [64 q] dwords
-  static constexpr int DO = QS + 64 * 4;              // dO bf16 [64 q][D], swizzled chunks
-  static constexpr int DOT = DO + 64 * D * 2;         // dO^T bf16 [D][64 q], swizzled chunks
-  static constexpr int QT = DOT + D * 64 * 2;         // Q^T bf16 [D][64 q], swizzled chunks
-  static constexpr int ROWS = QT + D * 64 * 2;        // mq, il, D: 3 x [64] floats
-  static constexpr int PS = ROWS + 3 * 64 * 4;        // A = P~/l bf16 [64 keys][64 q], swizzled chunks
-  static constexpr int DS = PS + 64 * 64 * 2;         // dS bf16 [64 keys][64 q]
-  static constexpr int BYTES = DS + 64 * 64 * 2;
+  static constexpr int KEYS = 16 * W;                 // 32 keys per pair of waves
+  static constexpr int QC = 0;                        // A: Q^ codes [64 q][D/2]
+  static constexpr int QS = QC + 64 * D / 2;          // A: Q^ scales [64 q] dwords
+  static constexpr int ROWS = QS + 64 * 4;            // A: mq, il, D: 3 x [64] floats
+  static constexpr int DO = ROWS + 3 * 64 * 4;        // A: dO bf16 [64 q][D], swizzled chunks
+  static constexpr int DOT = DO + 64 * D * 2;         // B: dO^T bf16 [D][64 q], swizzled chunks
+  static constexpr int QT = DOT + D * 64 * 2;         // B: Q^T bf16 [D][64 q], swizzled chunks
+  static constexpr int PS = QT + D * 64 * 2;          // A = P~/l bf16 [KEYS][64 q], swizzled chunks
+  static constexpr int DS = PS + KEYS * 64 * 2;       // dS bf16 [KEYS][64 q]
+  static constexpr int BYTES = DS + KEYS * 64 * 2;
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int W, bool CAUSAL>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(BwdParams p) {
-  using L = DkdvLds<D>;
+  using L = DkdvLds<D, W>;
   constexpr int KS_STEPS = D / 64;        // FP4 k-steps of S^T
   constexpr int DS_STEPS = D / 16;        // bf16 k-steps of dP^T
   constexpr int CH = D / 2;               // channels accumulated per wave
   constexpr int CT = CH / 32;             // 32-channel tiles per wave
+  constexpr int RC = D / 8;               // 16-B chunks per dO row
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
 
   const int tid = threadIdx.x;
@@ -175,9 +181,9 @@ bwd_dkdv_kernel(BwdParams p) {
   const int pair = wave >> 1, half = wave & 1;
 
   const int64_t N = p.N;
-  const int64_t nkt = N / 64;
+  const int64_t nkt = N / L::KEYS;
   const int64_t bg = blockIdx.x / nkt;            // b * Hkv + g
-  const int64_t k0 = (blockIdx.x - bg * nkt) * 64;
+  const int64_t k0 = (blockIdx.x - bg * nkt) * L::KEYS;
   const int64_t b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int64_t group = p.Hq / p.Hkv;
   const int64_t kp = k0 + 32 * pair;              // the pair's first key
@@ -204,136 +210,201 @@ bwd_dkdv_kernel(BwdParams p) {
     dk[ct] = v16f{};
   }
 
+  // ---- staging jobs (one 64-lane LDS-DMA instruction each) ----
+  // group A: Q^ codes (1-KB pieces), dO (1-KB pieces), Q^ scales, mq, il, D; group B: dO^T, Q^T.
+  // The query heads of this KV head are contiguous, so one resource per tensor covers them; the
+  // tile's (head, row) offset goes in the scalar offset.
+  constexpr int NQC = 64 * D / 2 / 1024, NDO = 64 * D * 2 / 1024;
+  constexpr int NA = NQC + NDO + 4, NB = 2 * (D * 64 * 2 / 1024);
+  constexpr int JA = (NA + W - 1) / W, JB = (NB + W - 1) / W;
+  const int64_t hq0 = b * p.Hq + g * group;       // first query head of this KV head
+  const auto qc_rs = make_rsrc(p.q_codes + hq0 * N * (D / 2), group * N * (D / 2));
+  const auto qs_rs = make_rsrc(p.q_scales + hq0 * N * (D / 32), group * N * (D / 32));
+  const auto do_rs = make_rsrc(p.dout + hq0 * N * D, group * N * D * 2);
+  const auto mq_rs = make_rsrc(p.mq + hq0 * N, group * N * 4);
+  const auto il_rs = make_rsrc(p.il + hq0 * N, group * N * 4);
+  const auto dl_rs = make_rsrc(p.delta + hq0 * N, group * N * 4);
+  const auto dot_rs = make_rsrc(p.dot + hq0 * D * N, group * D * N * 2);
+  const auto qt_rs = make_rsrc(p.qt + hq0 * D * N, group * D * N * 2);
+  // kinds: 0 Q^ codes, 1 dO, 2 Q^ scales, 3 mq, 4 il, 5 D | 6 dO^T, 7 Q^T
+  auto kind_a = [](int j) constexpr { return j < NQC ? 0 : j < NQC + NDO ? 1 : 2 + (j - NQC - NDO); };
+  auto kind_b = [](int j) constexpr { return j < NB / 2 ? 6 : 7; };
+  auto goff_of = [&](int kind, int j) -> uint32_t {   // lane's global byte offset within the tile
+    if (kind == 0) return 16 * (64 * j + lane);
+    if (kind == 1) {
+      const int cidx = 64 * (j - NQC) + lane, q = cidx / RC, cc = (cidx % RC) ^ swz_big(q, RC);
+      return q * (D * 2) + 16 * cc;
+    }
+    if (kind == 2) return lane * (D / 32);
+    if (kind <= 5) return 4 * lane;
+    const int cidx = 64 * (kind == 6 ? j : j - NB / 2) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
+    return (uint32_t)ch * (uint32_t)(N * 2) + 16 * cc;
+  };
+  auto dst_of = [](int kind, int j) -> int {
+    return kind == 0 ? L::QC + 1024 * j : kind == 1 ? L::DO + 1024 * (j - NQC) : kind == 2 ? L::QS
+         : kind <= 5 ? L::ROWS + 256 * (kind - 3) : kind == 6 ? L::DOT + 1024 * j : L::QT + 1024 * (j - NB / 2);
+  };
+  constexpr bool PRE_A = JA <= 6, PRE_B = JB <= 6;
+  uint32_t goff_a[PRE_A ? JA : 1], goff_b[PRE_B ? JB : 1];
+  if constexpr (PRE_A) {
+#pragma unroll
+    for (int i = 0; i < JA; ++i) { const int j = min(wave + W * i, NA - 1); goff_a[i] = goff_of(kind_a(j), j); }
+  }
+  if constexpr (PRE_B) {
+#pragma unroll
+    for (int i = 0; i < JB; ++i) { const int j = min(wave + W * i, NB - 1); goff_b[i] = goff_of(kind_b(j), j); }
+  }
+  // row offsets of query tile (hh, q0) in elements: along the rows of [head][N] and of [head][D][N]
+  auto issue = [&](int kind, int j, uint32_t goff, int64_t hh, int64_t q0) __attribute__((always_inline)) {
+    auto* dst = (__attribute__((address_space(3))) void*)(smem + dst_of(kind, j));   // LDS-DMA target
+    const int r = __builtin_amdgcn_readfirstlane((int)(hh * N + q0));                  // row of [head][N]
+    const int tcol = __builtin_amdgcn_readfirstlane((int)(hh * D * N + q0));          // element of [head][D][N]
+    switch (kind) {
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(qc_rs, dst, 16, (int)goff, r * (D / 2), 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(do_rs, dst, 16, (int)goff, r * (D * 2), 0, 0); break;
+      case 2:
+        if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 4, (int)goff, r * (D / 32), 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 2, (int)goff, r * (D / 32), 0, 0);
+        break;
+      case 3: __builtin_amdgcn_raw_ptr_buffer_load_lds(mq_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
+      case 4: __builtin_amdgcn_raw_ptr_buffer_load_lds(il_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
+      case 5: __builtin_amdgcn_raw_ptr_buffer_load_lds(dl_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
+      case 6: __builtin_amdgcn_raw_ptr_buffer_load_lds(dot_rs, dst, 16, (int)goff, tcol * 2, 0, 0); break;
+      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(qt_rs, dst, 16, (int)goff, tcol * 2, 0, 0); break;
+    }
+  };
+  auto issue_a = [&](int64_t hh, int64_t q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < JA; ++i) {
+      const int j = min(wave + W * i, NA - 1);
+      uint32_t goff;
+      if constexpr (PRE_A) goff = goff_a[PRE_A ? i : 0];
+      else goff = goff_of(kind_a(j), j);
+      issue(kind_a(j), j, goff, hh, q0);
+    }
+  };
+  auto issue_b = [&](int64_t hh, int64_t q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < JB; ++i) {
+      const int j = min(wave + W * i, NB - 1);
+      uint32_t goff;
+      if constexpr (PRE_B) goff = goff_b[PRE_B ? i : 0];
+      else goff = goff_of(kind_b(j), j);
+      issue(kind_b(j), j, goff, hh, q0);
+    }
+  };
+
+  // ---- tiles: the query heads of the group, and per head the query tiles that see any key ----
   const int64_t j_first = CAUSAL ? k0 / 64 : 0;   // query tiles below the keys see none of them
-  for (int64_t hh = 0; hh < group; ++hh) {
+  const int64_t nj = N / 64 - j_first;
+  const int64_t ntile = group * nj;
+  issue_a(0, j_first * 64);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int64_t n = 0; n < ntile; ++n) {
+    const int64_t hh = n / nj;
+    const int64_t q0 = (j_first + (n - hh * nj)) * 64;
     const int64_t h = g * group + hh;
     const int64_t bh = b * p.Hq + h;
-    for (int64_t j = j_first; j < nkt; ++j) {
-      const int64_t q0 = j * 64;
-      // ---- stage the query tile: 64 rows of Q^ codes/scales, dO, dO^T, Q^T and row constants ----
-      {
-        const uint8_t* qc = p.q_codes + (bh * N + q0) * (D / 2);
-        for (int ci = tid; ci < 64 * D / 32; ci += 256)
-          *reinterpret_cast<v4i*>(smem + L::QC + 16 * ci) = *reinterpret_cast<const v4i*>(qc + 16 * ci);
-        if (tid < 64) {
-          const uint8_t* qs = p.q_scales + (bh * N + q0 + tid) * (D / 32);
-          *reinterpret_cast<uint32_t*>(smem + L::QS + 4 * tid) =
-              (D == 128) ? *reinterpret_cast<const uint32_t*>(qs) : (uint32_t)*reinterpret_cast<const uint16_t*>(qs);
-        } else if (tid < 128) {
-          const int r = tid - 64;
-          reinterpret_cast<float*>(smem + L::ROWS)[r] = p.mq[bh * N + q0 + r];
-          reinterpret_cast<float*>(smem + L::ROWS)[64 + r] = p.il[bh * N + q0 + r];
-          reinterpret_cast<float*>(smem + L::ROWS)[128 + r] = p.delta[bh * N + q0 + r];
-        }
-        constexpr int RC = D / 8;               // 16-B chunks per dO row
-        for (int ci = tid; ci < 64 * RC; ci += 256) {
-          const int q = ci / RC, cc = ci % RC;
-          *reinterpret_cast<v4i*>(smem + L::DO + q * 2 * D + 16 * (cc ^ swz_big(q, RC))) =
-              *reinterpret_cast<const v4i*>(p.dout + (bh * N + q0 + q) * D + 8 * cc);
-        }
-        for (int ci = tid; ci < D * 8; ci += 256) {
-          const int ch = ci >> 3, cc = ci & 7;
-          const int64_t off = (bh * D + ch) * N + q0 + 8 * cc;
-          *reinterpret_cast<v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
-              *reinterpret_cast<const v4i*>(p.dot + off);
-          *reinterpret_cast<v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8))) =
-              *reinterpret_cast<const v4i*>(p.qt + off);
-        }
-      }
-      __syncthreads();
+    (void)bh;
+    issue_b(hh, q0);
 
-      // ---- elementwise phase: keys kp + [0,32) x queries q0 + 32 half + [0,32) ----
-      {
-        const int ql = 32 * half + l32;                  // this lane's query within the tile
-        const int64_t qrow = q0 + ql;
-        // S^T = K^ Q^T (FP4)
-        const uint8_t* qcl = smem + L::QC + ql * (D / 2);
-        const uint32_t qsw = *reinterpret_cast<const uint32_t*>(smem + L::QS + 4 * ql);
-        const int qsc = (int)(qsw >> (8 * hi));
-        v16f st = v16f{};
-        st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi)),
-                                                            st, 4, 4, 0, ksc, 0, qsc);
-        if (KS_STEPS == 2)
-          st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              widen(ka[KS_STEPS - 1]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi + 32)), st, 4, 4, 2, ksc, 2, qsc);
-        // dP^T = V^ dO^T (bf16)
-        v16f dp = v16f{};
+    // ---- elementwise phase: keys kp + [0,32) x queries q0 + 32 half + [0,32) ----
+    {
+      const int ql = 32 * half + l32;                  // this lane's query within the tile
+      const int64_t qrow = q0 + ql;
+      // S^T = K^ Q^T (FP4)
+      const uint8_t* qcl = smem + L::QC + ql * (D / 2);
+      const uint32_t qsw = *reinterpret_cast<const uint32_t*>(smem + L::QS + 4 * ql);
+      const int qsc = (int)(qsw >> (8 * hi));
+      v16f st = v16f{};
+      st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi)),
+                                                          st, 4, 4, 0, ksc, 0, qsc);
+      if (KS_STEPS == 2)
+        st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            widen(ka[KS_STEPS - 1]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi + 32)), st, 4, 4, 2, ksc, 2, qsc);
+      // dP^T = V^ dO^T (bf16)
+      v16f dp = v16f{};
 #pragma unroll
-        for (int s = 0; s < DS_STEPS; ++s) {
-          const int cc = 2 * s + hi;
-          const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, D / 8)));
-          dp = mfma_bf16(va[s], bo, dp);
-        }
-        const float mq = reinterpret_cast<const float*>(smem + L::ROWS)[ql];
-        const float il = reinterpret_cast<const float*>(smem + L::ROWS)[64 + ql];
-        const float dd = reinterpret_cast<const float*>(smem + L::ROWS)[128 + ql];
-        // register r holds key kp + 16 hi + r
-        if (CAUSAL) {
-          const int jrel = (int)(qrow - kp) - 16 * hi;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r > jrel) st[r] = -__builtin_inff();
-        }
-        float mx = st[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        const int sb = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
-        const float sc = __uint_as_float((uint32_t)sb << 23);
-        float pr[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -mq));
-        uint32_t aw[8], sw8[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t u = 0;
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q], pr[4 * q + 1], sc, 0);
-          u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
-          const v2f a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 0);   // P~ (dequantized)
-          const v2f a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 1);
-          aw[2 * q] = pk_bf16(a0[0] * il, a0[1] * il);
-          aw[2 * q + 1] = pk_bf16(a1[0] * il, a1[1] * il);
-          float ds[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ds[i] = pr[4 * q + i] * il * (dp[4 * q + i] - dd);
-          sw8[2 * q] = pk_bf16(ds[0], ds[1]);
-          sw8[2 * q + 1] = pk_bf16(ds[2], ds[3]);
-        }
-        // [key][query] scratch: key row 32 pair + 16 hi + r, query column ql
-        uint16_t* ps = reinterpret_cast<uint16_t*>(smem + L::PS);
-        uint16_t* dsp = reinterpret_cast<uint16_t*>(smem + L::DS);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * pair + 16 * hi + r;
-          const int col = 8 * ((ql >> 3) ^ swz_big(key, 8)) + (ql & 7);
-          const uint32_t a = aw[r >> 1], s2 = sw8[r >> 1];
-          ps[key * 64 + col] = (uint16_t)((r & 1) ? (a >> 16) : (a & 0xFFFF));
-          dsp[key * 64 + col] = (uint16_t)((r & 1) ? (s2 >> 16) : (s2 & 0xFFFF));
-        }
+      for (int s = 0; s < DS_STEPS; ++s) {
+        const int cc = 2 * s + hi;
+        const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, RC)));
+        dp = mfma_bf16(va[s], bo, dp);
       }
-      __syncthreads();
-
-      // ---- products: dV^T += dO^T A, dK^T += Q^T dS over the tile's 64 queries ----
-      {
-        const int key = 32 * pair + l32;
+      const float mq = reinterpret_cast<const float*>(smem + L::ROWS)[ql];
+      const float il = reinterpret_cast<const float*>(smem + L::ROWS)[64 + ql];
+      const float dd = reinterpret_cast<const float*>(smem + L::ROWS)[128 + ql];
+      // register r holds key kp + 16 hi + r
+      if (CAUSAL) {
+        const int jrel = (int)(qrow - kp) - 16 * hi;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int cc = 2 * s + hi;                    // queries 16 s + 8 hi + [0, 8)
-          const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
-          const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const int ch = CH * half + 32 * ct + l32;
-            const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
-            const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
-            dv[ct] = mfma_bf16(ao, bp, dv[ct]);
-            dk[ct] = mfma_bf16(aq, bs, dk[ct]);
-          }
-        }
+        for (int r = 0; r < 16; ++r)
+          if (r > jrel) st[r] = -__builtin_inff();
       }
-      __syncthreads();
+      float mx = st[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const int sb = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
+      const float sc = __uint_as_float((uint32_t)sb << 23);
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -mq));
+      uint32_t aw[8], sw8[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t u = 0;
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q], pr[4 * q + 1], sc, 0);
+        u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
+        const v2f a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 0);   // P~ (dequantized)
+        const v2f a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 1);
+        aw[2 * q] = pk_bf16(a0[0] * il, a0[1] * il);
+        aw[2 * q + 1] = pk_bf16(a1[0] * il, a1[1] * il);
+        float ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[i] = pr[4 * q + i] * il * (dp[4 * q + i] - dd);
+        sw8[2 * q] = pk_bf16(ds[0], ds[1]);
+        sw8[2 * q + 1] = pk_bf16(ds[2], ds[3]);
+      }
+      // [key][query] scratch: key row 32 pair + 16 hi + r, query column ql
+      uint16_t* ps = reinterpret_cast<uint16_t*>(smem + L::PS);
+      uint16_t* dsp = reinterpret_cast<uint16_t*>(smem + L::DS);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * pair + 16 * hi + r;
+        const int col = 8 * ((ql >> 3) ^ swz_big(key, 8)) + (ql & 7);
+        const uint32_t a = aw[r >> 1], s2 = sw8[r >> 1];
+        ps[key * 64 + col] = (uint16_t)((r & 1) ? (a >> 16) : (a & 0xFFFF));
+        dsp[key * 64 + col] = (uint16_t)((r & 1) ? (s2 >> 16) : (s2 & 0xFFFF));
+      }
     }
+    // group B of this tile has landed (each wave waits for its own loads); group A is free
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (n + 1 < ntile) {
+      const int64_t hn = (n + 1) / nj;
+      issue_a(hn, (j_first + (n + 1 - hn * nj)) * 64);
+    }
+
+    // ---- products: dV^T += dO^T A, dK^T += Q^T dS over the tile's 64 queries ----
+    {
+      const int key = 32 * pair + l32;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int cc = 2 * s + hi;                    // queries 16 s + 8 hi + [0, 8)
+        const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
+        const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int ch = CH * half + 32 * ct + l32;
+          const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+          const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+          dv[ct] = mfma_bf16(ao, bp, dv[ct]);
+          dk[ct] = mfma_bf16(aq, bs, dk[ct]);
+        }
+      }
+    }
+    // group A of the next tile has landed; group B and the scratch are free
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // ---- store: lane holds key kp + l32, channels CH half + 32 ct + 8 a + 4 hi + [0,4) ----
@@ -599,8 +670,12 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((p.N / 64) * p.Hkv * p.B)), dim3(256), 0,
-                     stream, p);
+  if (p.N % 128 == 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8, CAUSAL>), dim3((unsigned)((p.N / 128) * p.Hkv * p.B)), dim3(512), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, CAUSAL>), dim3((unsigned)((p.N / 64) * p.Hkv * p.B)), dim3(256), 0,
+                       stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.N % 256 == 0) {

@@ -122,6 +122,8 @@ int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
       a->workspace_bytes < ws.total)
     return ATTN_FP4_E_WORKSPACE;
   if (a->B * a->Hq > 65535) return ATTN_FP4_E_INVALID_ARG;   // grid z of the transposes
+  // the kernels address one KV head's query-head group of bf16 [N, d] tensors with 32-bit offsets
+  if ((a->Hq / a->Hkv) * a->N * a->d * 2 > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_UNSUPPORTED;
   st = check_device();
   if (st != ATTN_FP4_OK) return st;
   attnfp4::BwdParams p;

@@ -167,7 +167,9 @@ int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
  * l); dQ, dK, dV come from bf16 matrix-core products with fp32
  * accumulation, gradients passing straight through the quantizers.
  * Errors: as attn_fp4_fwd, plus ATTN_FP4_E_WORKSPACE, and
- * ATTN_FP4_E_UNSUPPORTED for combinations this build does not implement.
+ * ATTN_FP4_E_UNSUPPORTED when (Hq / Hkv) * N * d * 2 bytes (one KV head's
+ * group of bf16 [N, d] tensors) exceeds 2^31 - 1, the reach of the kernels'
+ * 32-bit buffer offsets.
  */
 int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* args, void* stream);
 

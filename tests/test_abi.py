@@ -61,6 +61,11 @@ def test_host_validation_rejects_before_launch():
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0
     b = ops.BwdArgs(p, p, p, p, p, p, p, p, p, p, p, p, p, None, 0, 1, 2, 2, 128, 128, 0, 0.0)
     assert L.attn_fp4_bwd_recompute(ctypes.byref(b), None) == 5   # workspace missing
+    # a KV head's group of bf16 [N, d] tensors beyond 2^31 bytes: unsupported (32-bit offsets)
+    B, Hq, Hkv, N, d = 1, 64, 1, 1 << 18, 128
+    need = L.attn_fp4_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    b = ops.BwdArgs(p, p, p, p, p, p, p, p, p, p, p, p, p, ctypes.c_void_p(1 << 20), need, B, Hq, Hkv, N, d, 0, 0.0)
+    assert L.attn_fp4_bwd_recompute(ctypes.byref(b), None) == 3
 
 
 def test_binding_raises_without_library(monkeypatch):

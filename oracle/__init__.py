@@ -26,6 +26,7 @@ that each step can be checked by eye against the pages it follows:
 Parity status of each function is stated in its module header.
 """
 
+from .efq import EFQ_A, EFQ_B, efq_block_exponent, efq_codes, efq_fake_quant  # noqa: F401
 from .mx import (  # noqa: F401
     E2M1_GRID,
     MX_BLOCK,

@@ -52,6 +52,7 @@ D = rowsum(P o dP) with quantizers off.
 
 import numpy as np
 
+from .efq import efq_fake_quant
 from .mx import fake_quant_mx
 
 BC = 64  # key-tile width; part of the definition of P quantization
@@ -91,14 +92,18 @@ def softmax_attention(q, k, v, causal=False, scale=None):
     return out
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None):
+def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp"):
     """Tile-by-tile fake-quantized attention forward.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (values read exactly as float64).
     rows: optional 1-D array of query rows to compute (rows are independent).
     quant=False replaces all four quantizers by the identity.
+    p_rule: "exp" -- P~ = MXFP4(exp(s - m)) (exp-then-quantize, the definition); "efq" -- P~ from
+    the EFQ-Softmax codes of the shifted scores (oracle/efq.py, a reading of the pages).
     Returns (O [B, Hq, R, d], m [B, Hq, R], l [B, Hq, R]), float64.
     """
+    if p_rule not in ("exp", "efq"):
+        raise ValueError("p_rule must be 'exp' or 'efq'")
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     B, Hq, Hkv, N, d = _check_shapes(q, k, v)
     if N % bc:
@@ -131,8 +136,11 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None):
                         s = np.where(keys[None, :] <= rows[act][:, None], s, -np.inf)
                     m_old = m[act]
                     m_new = np.maximum(m_old, s.max(axis=1))
-                    p = np.exp(s - m_new[:, None])
-                    p_tilde = fq(p, axis=-1)
+                    if p_rule == "efq" and quant:
+                        p_tilde = efq_fake_quant((s - m_new[:, None]) / np.log(2.0), axis=-1)
+                    else:
+                        p = np.exp(s - m_new[:, None])
+                        p_tilde = fq(p, axis=-1)
                     alpha = np.where(np.isneginf(m_old), 0.0, np.exp(m_old - m_new))
                     l[act] = alpha * l[act] + p_tilde.sum(axis=1)
                     acc[act] = alpha[:, None] * acc[act] + p_tilde @ v_hat[keys]

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -80,6 +80,7 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
   if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
+  if (a->p_rule != ATTN_FP4_P_EXP && a->p_rule != ATTN_FP4_P_EFQ) return ATTN_FP4_E_INVALID_ARG;
   st = check_device();
   if (st != ATTN_FP4_OK) return st;
   attnfp4::FwdParams p;
@@ -99,7 +100,7 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
   const double s = resolve_scale(a->softmax_scale, a->d);
   p.c = (float)(s * 1.4426950408889634);
   p.scale_nat = (float)s;
-  hipError_t e = attnfp4::launch_fwd(p, (int)a->d, a->causal != 0, (hipStream_t)stream);
+  hipError_t e = attnfp4::launch_fwd(p, (int)a->d, a->causal != 0, a->p_rule == ATTN_FP4_P_EFQ, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
 }
 

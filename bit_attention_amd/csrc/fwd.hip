@@ -71,7 +71,7 @@ __device__ __forceinline__ int slot_key(int s) {
 template <int D, int W>
 constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
 
-template <int D, int W, bool CAUSAL>
+template <int D, int W, bool CAUSAL, bool EFQ>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W>(), waves_per_simd<D, W>())))
 fwd_kernel(FwdParams p) {
@@ -268,6 +268,28 @@ fwd_kernel(FwdParams p) {
     // already the B operand of the PV MFMA (lane l: keys 32(l/32) .. +31 of query l%32)
     const float mc = m_new * c;
     uint32_t pk[2][2];
+    if constexpr (EFQ) {
+      // exp-free codes: k = clamp(rne(A y + B), 0, 7) with y = x - e, x = s c - m c = log2 p and
+      // e = psc - 127; one FMA per score: A y + B = s (A c) + (B - A (m c + e)).  A, B: the
+      // least-squares line through (log2 v, k) of the non-zero E2M1 magnitudes v.
+      constexpr float kA = 1.7470566f, kB = 2.3141184f;
+      const float ac = kA * c, tb = kB - kA * (mc + (float)(psc - 127));
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+          uint32_t ev = 0, od = 0;   // bytes: codes of the even / odd keys of the 8
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // v_cvt_pk_u8_f32 rounds half to even; the clamp to [-1, 7] keeps -inf (masked) at 0
+            const float t0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(sT[T][8 * hw + 2 * i], ac, tb), -1.0f, 7.0f);
+            const float t1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(sT[T][8 * hw + 2 * i + 1], ac, tb), -1.0f, 7.0f);
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(t0, i, ev);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(t1, i, od);
+          }
+          pk[T][hw] = ev | (od << 4);
+        }
+    } else {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
 #pragma unroll
@@ -281,6 +303,7 @@ fwd_kernel(FwdParams p) {
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, e[6], e[7], sc, 3);
         pk[T][hw] = u;
       }
+    }
     }
     const v8i pb = v8i{(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1], 0, 0, 0, 0};
 
@@ -363,24 +386,25 @@ fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, int W, bool CAUSAL>
+template <int D, int W, bool CAUSAL, bool EFQ>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t blocks = (p.N / (32 * W)) * p.Hq * p.B;
-  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL, EFQ>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool EFQ>
 hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
   // four waves (128 rows) per workgroup when the rows tile evenly, else two (N % 64 == 0)
-  if (p.N % 128 == 0) return causal ? launch<D, 4, true>(p, stream) : launch<D, 4, false>(p, stream);
-  return causal ? launch<D, 2, true>(p, stream) : launch<D, 2, false>(p, stream);
+  if (p.N % 128 == 0) return causal ? launch<D, 4, true, EFQ>(p, stream) : launch<D, 4, false, EFQ>(p, stream);
+  return causal ? launch<D, 2, true, EFQ>(p, stream) : launch<D, 2, false, EFQ>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-  return d == 128 ? launch_d<128>(p, causal, stream) : launch_d<64>(p, causal, stream);
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream) {
+  if (efq) return d == 128 ? launch_d<128, true>(p, causal, stream) : launch_d<64, true>(p, causal, stream);
+  return d == 128 ? launch_d<128, false>(p, causal, stream) : launch_d<64, false>(p, causal, stream);
 }
 
 }  // namespace attnfp4

@@ -57,7 +57,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
 
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
                            void* scales, hipStream_t stream);
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace attnfp4

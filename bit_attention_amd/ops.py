@@ -49,7 +49,11 @@ class FwdArgs(ctypes.Structure):
         ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
         ("N", ctypes.c_int64), ("d", ctypes.c_int64),
         ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("p_rule", ctypes.c_int32),
     ]
+
+
+P_EXP, P_EFQ = 0, 1   # P~ rules of the forward (exp-then-quantize; exp-free EFQ codes)
 
 
 class BwdArgs(ctypes.Structure):
@@ -148,7 +152,7 @@ def attn_fp4_quantize(x, axis, codes=None, scales=None, stream=None):
 
 
 def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal=False,
-                 softmax_scale=0.0, o=None, m=None, l=None, stream=None):
+                 softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP):
     """MXFP4 attention forward on pre-quantized operands (layouts of attn_fp4_quantize).
 
     q_codes [B, Hq, N, d/2]; k_codes [B, Hkv, N, d/2]; v_codes [B, Hkv, N/32, d, 16].
@@ -173,7 +177,7 @@ def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal
     if l is None:
         l = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     a = FwdArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
-                _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale))
+                _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale), int(p_rule))
     _check(lib().attn_fp4_fwd(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd")
     return o, m, l
 

@@ -115,7 +115,24 @@ typedef struct {
   int64_t B, Hq, Hkv, N, d;
   int32_t causal;
   float softmax_scale;
+  int32_t p_rule;     /* how P~ is formed, see ATTN_FP4_P_* */
 } attn_fp4_fwd_args;
+
+/*
+ * P~ rules of the forward:
+ *   ATTN_FP4_P_EXP  exp-then-quantize (the method's definition): P~ = MXFP4 of
+ *                   p = exp(s - m) per 32-key block.
+ *   ATTN_FP4_P_EFQ  exp-free codes after the EFQ-Softmax abstract, in this
+ *                   library's reading (the pages give no formula): per block
+ *                   the same E8M0 exponent e from the block maximum, then code
+ *                   k = clamp(round_half_even(A y + B), 0, 7) of the residual
+ *                   y = log2(p) - e computed from the shifted score without an
+ *                   exponential; A = 1.7470566, B = 2.3141184 is the
+ *                   least-squares line through (log2 v, k) of the seven
+ *                   non-zero E2M1 magnitudes v.  attn_fp4_bwd_recompute
+ *                   implements the exp rule only.
+ */
+enum { ATTN_FP4_P_EXP = 0, ATTN_FP4_P_EFQ = 1 };
 
 /*
  * attn_fp4_fwd -- MXFP4 attention forward (Attn-QAT FP4 forward; EFQ-Softmax

@@ -30,7 +30,7 @@ QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 # Measured HBM traffic of one forward launch at the bench shape: rocprofv3 --pmc FETCH_SIZE and
 # --pmc WRITE_SIZE, each scaled by the factor the same counter shows on a plain 1 GiB device copy
 # (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source it was measured on.
-FWD_TRAFFIC = {"source_sha1": "a89d9c8742bf143d9b02e38c4e9bb5e2aebb17b0", "bytes": 1.056e9}
+FWD_TRAFFIC = {"source_sha1": "09ad48f5849896b1a3bebc8424b42ac5cc5c026e", "bytes": 1.057e9}
 
 
 def fwd_source_sha1():

@@ -43,6 +43,7 @@ from .attention import (  # noqa: F401
     BC,
     softmax_attention,
     attn_fwd,
+    attn_fwd_kvcache,
     attn_bwd,
     attn_row_max,
 )

@@ -29,6 +29,13 @@ are scaled before the max and exp is the natural exponential; causal masking
 is top-left aligned (key j visible iff j <= i); query head h uses KV head
 h // (Hq // Hkv).
 
+Cache forward (`attn_fwd_kvcache`: FP4 attention for LLM inference, where the
+new rows of a sequence attend to keys and values quantized once and kept):
+the same tile loop for Nq new rows placed at the last Nq positions of each
+sequence (bottom-right causal alignment), over a cache of per-sequence length
+L_b, with V^ quantized over the cache's whole capacity in 32-token blocks
+from position 0.  A row that sees no key gives O = 0, m = -inf, l = 0.
+
 Backward (Attn-QAT abstract: scores recomputed with the same FP4 QK^T as
 the forward; the D term taken from the FP4 forward's own output).  With the
 forward's final m, l per row and straight-through gradients for the four
@@ -47,7 +54,11 @@ quantizers on -> the direct formula; Q = 0 -> mean of V^ (causal: prefix
 mean); identical V^ rows -> that row; V -> 2^k V scales O exactly;
 quantizers off -> float64 autograd of textbook attention and central finite
 differences; Q = 0 with quantizers on -> autograd at (Q^, K^, V^);
-D = rowsum(P o dP) with quantizers off.
+D = rowsum(P o dP) with quantizers off.  Cache forward
+(tests/test_oracle_kvcache.py): quantizers off -> textbook attention over
+the visible keys; quantizers on -> rows of the full forward at those
+positions; Q = 0 -> mean of V^ over the visible keys (ragged lengths); empty
+rows; cache contents past the length have no effect.
 """
 
 import numpy as np
@@ -92,6 +103,40 @@ def softmax_attention(q, k, v, causal=False, scale=None):
     return out
 
 
+def _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant):
+    """The tile loop for R query rows of one head: row r sees keys 0 .. limit[r] (none if < 0).
+
+    q_hat [R, d], k_hat, v_hat [Nk, d] (already quantized, Nk a multiple of bc).  A tile is
+    visited by the rows that see at least its first key; keys past a row's limit are masked.
+    A row that sees no key gets O = 0, m = -inf, l = 0.  Returns (O [R, d], m [R], l [R]).
+    """
+    R, d = q_hat.shape
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, d))
+    last = int(limit.max()) if R else -1
+    for t in range(last // bc + 1 if last >= 0 else 0):
+        keys = np.arange(t * bc, (t + 1) * bc)
+        act = limit >= t * bc
+        if not act.any():
+            continue
+        s = (q_hat[act] @ k_hat[keys].T) * scale
+        s = np.where(keys[None, :] <= limit[act][:, None], s, -np.inf)
+        m_old = m[act]
+        m_new = np.maximum(m_old, s.max(axis=1))
+        if p_rule == "efq" and quant:
+            p_tilde = efq_fake_quant((s - m_new[:, None]) / np.log(2.0), axis=-1)
+        else:
+            p = np.exp(s - m_new[:, None])
+            p_tilde = fq(p, axis=-1)
+        alpha = np.where(np.isneginf(m_old), 0.0, np.exp(m_old - m_new))
+        l[act] = alpha * l[act] + p_tilde.sum(axis=1)
+        acc[act] = alpha[:, None] * acc[act] + p_tilde @ v_hat[keys]
+        m[act] = m_new
+    O = np.where(l[:, None] > 0, acc / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return O, m, l
+
+
 def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp"):
     """Tile-by-tile fake-quantized attention forward.
 
@@ -116,38 +161,62 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_
     O = np.empty((B, Hq, R, d))
     M = np.empty((B, Hq, R))
     L = np.empty((B, Hq, R))
+    # causal: row i sees keys 0 .. i (top-left alignment); otherwise all N keys
+    limit = rows.copy() if causal else np.full(R, N - 1, dtype=np.int64)
     for b in range(B):
         for g in range(Hkv):
             k_hat = fq(k[b, g], axis=-1)          # along the head dim
             v_hat = fq(v[b, g], axis=0)           # along the sequence
             for h in range(g * group, (g + 1) * group):
                 q_hat = fq(q[b, h][rows], axis=-1)
-                m = np.full(R, -np.inf)
-                l = np.zeros(R)
-                acc = np.zeros((R, d))
-                for t in range(N // bc):
-                    keys = np.arange(t * bc, (t + 1) * bc)
-                    # causal: the tile is visited only by rows at or past its first key
-                    act = rows >= t * bc if causal else np.ones(R, dtype=bool)
-                    if not act.any():
-                        continue
-                    s = (q_hat[act] @ k_hat[keys].T) * scale
-                    if causal:
-                        s = np.where(keys[None, :] <= rows[act][:, None], s, -np.inf)
-                    m_old = m[act]
-                    m_new = np.maximum(m_old, s.max(axis=1))
-                    if p_rule == "efq" and quant:
-                        p_tilde = efq_fake_quant((s - m_new[:, None]) / np.log(2.0), axis=-1)
-                    else:
-                        p = np.exp(s - m_new[:, None])
-                        p_tilde = fq(p, axis=-1)
-                    alpha = np.where(np.isneginf(m_old), 0.0, np.exp(m_old - m_new))
-                    l[act] = alpha * l[act] + p_tilde.sum(axis=1)
-                    acc[act] = alpha[:, None] * acc[act] + p_tilde @ v_hat[keys]
-                    m[act] = m_new
-                O[b, h] = acc / l[:, None]
-                M[b, h] = m
-                L[b, h] = l
+                O[b, h], M[b, h], L[b, h] = _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant)
+    return O, M, L
+
+
+def attn_fwd_kvcache(q, k_cache, v_cache, seqlens=None, causal=False, scale=None, bc=BC,
+                     quant=True, rows=None, p_rule="exp"):
+    """Forward of Nq new query rows against a cache of keys and values (chunked prefill, decode).
+
+    q: [B, Hq, Nq, d], the queries of the last Nq positions of each sequence;
+    k_cache, v_cache: [B, Hkv, Nk, d], Nk a multiple of bc (the cache capacity);
+    seqlens: [B] valid cache lengths L_b in [0, Nk] (default Nk); the new rows' keys and values
+    are already in the cache, so query i sits at position L_b - Nq + i.
+    K^ is quantized per row along d and V^ along the sequence over the whole capacity, in
+    32-token blocks from position 0, exactly as the cache itself would be quantized.
+    Visible keys: j < L_b, and with causal also j <= L_b - Nq + i (bottom-right alignment).  A row
+    that sees no key (causal, L_b - Nq + i < 0, or L_b = 0) gives O = 0, m = -inf, l = 0.
+    With Nq = Nk = L_b this is `attn_fwd`.  Returns (O [B, Hq, R, d], m, l [B, Hq, R]).
+    """
+    if p_rule not in ("exp", "efq"):
+        raise ValueError("p_rule must be 'exp' or 'efq'")
+    q, k_cache, v_cache = (np.asarray(t, dtype=np.float64) for t in (q, k_cache, v_cache))
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d or Hq % Hkv:
+        raise ValueError("k_cache and v_cache must be [B, Hkv, Nk, d] matching q")
+    if Nk % bc:
+        raise ValueError("the cache capacity must be a multiple of the tile width")
+    seqlens = np.full(B, Nk, dtype=np.int64) if seqlens is None else np.asarray(seqlens, dtype=np.int64)
+    if seqlens.shape != (B,) or (seqlens < 0).any() or (seqlens > Nk).any():
+        raise ValueError("seqlens must be [B] with values in [0, Nk]")
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    fq = fake_quant_mx if quant else _identity
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    group = Hq // Hkv
+    O = np.empty((B, Hq, R, d))
+    M = np.empty((B, Hq, R))
+    L = np.empty((B, Hq, R))
+    for b in range(B):
+        Lb = int(seqlens[b])
+        limit = (Lb - Nq + rows) if causal else np.full(R, Lb - 1, dtype=np.int64)
+        limit = np.minimum(limit, Lb - 1)
+        for g in range(Hkv):
+            k_hat = fq(k_cache[b, g], axis=-1)
+            v_hat = fq(v_cache[b, g], axis=0)
+            for h in range(g * group, (g + 1) * group):
+                q_hat = fq(q[b, h][rows], axis=-1)
+                O[b, h], M[b, h], L[b, h] = _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant)
     return O, M, L
 
 

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,10 +97,56 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
   p.N = a->N;
+  p.Nq = a->N;
+  p.Nk = a->N;
+  p.seqlens = nullptr;
   const double s = resolve_scale(a->softmax_scale, a->d);
   p.c = (float)(s * 1.4426950408889634);
   p.scale_nat = (float)s;
   hipError_t e = attnfp4::launch_fwd(p, (int)a->d, a->causal != 0, a->p_rule == ATTN_FP4_P_EFQ, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Nq <= 0 || a->Nk <= 0) return ATTN_FP4_E_INVALID_ARG;
+  if (a->d != 64 && a->d != 128) return ATTN_FP4_E_INVALID_ARG;
+  if (a->Nk % 64 != 0 || a->Hq % a->Hkv != 0) return ATTN_FP4_E_INVALID_ARG;
+  // 32-bit buffer offsets within one KV head's cache, and the grid: at most one workgroup per
+  // 64 packed query rows
+  if (a->Nk * a->d > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  if ((a->Nq * (a->Hq / a->Hkv) + 63) / 64 * a->Hkv * a->B > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  const void* ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes,
+                        a->v_scales, a->o, a->m, a->l};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
+  if (a->seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(a->seqlens_k) & 3u) != 0) return ATTN_FP4_E_INVALID_ARG;
+  if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
+  if (a->p_rule != ATTN_FP4_P_EXP && a->p_rule != ATTN_FP4_P_EFQ) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  attnfp4::FwdParams p;
+  p.q_codes = (const uint8_t*)a->q_codes;
+  p.q_scales = (const uint8_t*)a->q_scales;
+  p.k_codes = (const uint8_t*)a->k_codes;
+  p.k_scales = (const uint8_t*)a->k_scales;
+  p.v_codes = (const uint8_t*)a->v_codes;
+  p.v_scales = (const uint8_t*)a->v_scales;
+  p.o = (uint16_t*)a->o;
+  p.m = a->m;
+  p.l = a->l;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.N = 0;
+  p.Nq = a->Nq;
+  p.Nk = a->Nk;
+  p.seqlens = a->seqlens_k;
+  const double s = resolve_scale(a->softmax_scale, a->d);
+  p.c = (float)(s * 1.4426950408889634);
+  p.scale_nat = (float)s;
+  hipError_t e = attnfp4::launch_fwd_kvcache(p, (int)a->d, a->causal != 0, a->p_rule == ATTN_FP4_P_EFQ,
+                                             (hipStream_t)stream);
   return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
 }
 

@@ -71,7 +71,14 @@ __device__ __forceinline__ int slot_key(int s) {
 template <int D, int W>
 constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
 
-template <int D, int W, bool CAUSAL, bool EFQ>
+// KV selects the cache forward: Nq new query rows per head against a cache of capacity Nk per KV
+// head holding L_b valid keys for sequence b.  New row i sits at position L_b - Nq + i (causal
+// masking is bottom-right aligned), and the query heads that share a KV head are packed into the
+// waves' query columns, position-major (packed row = i * group + head within the group), so that
+// one pass over the cache serves the whole group.  Rows that see no key give O = 0, m = -inf,
+// l = 0; V^ blocks wholly past L_b take a unit scale, so that cache memory past the length,
+// whatever it holds, cannot turn the zero P~ of the masked keys into NaN.
+template <int D, int W, bool CAUSAL, bool EFQ, bool KV>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W>(), waves_per_simd<D, W>())))
 fwd_kernel(FwdParams p) {
@@ -96,36 +103,67 @@ fwd_kernel(FwdParams p) {
   const int hi = lane >> 5;
 
   // ---- work item: XCD-aware remap so that the workgroups of one head run on one XCD ----
-  const int64_t nqt = p.N / (32 * W);
-  const int64_t total = nqt * p.Hq * p.B;
+  const int64_t G = p.Hq / p.Hkv;                 // query heads per KV head
+  const int64_t nqt = KV ? (p.Nq * G + 32 * W - 1) / (32 * W) : p.N / (32 * W);
+  const int64_t total = nqt * (KV ? p.Hkv : p.Hq) * p.B;
   int64_t id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int64_t bh = id / nqt;
+  const int64_t bh = id / nqt;                    // (b, query head), cache forward: (b, KV head)
   int64_t qt = id - bh * nqt;
   if (CAUSAL) qt = nqt - 1 - qt;                  // longest rows first
-  const int64_t b = bh / p.Hq;
-  const int64_t h = bh - b * p.Hq;
-  const int64_t g = h / (p.Hq / p.Hkv);
-  const int64_t N = p.N;
-  const int64_t q0 = qt * 32 * W;
-  const int64_t qw = q0 + 32 * wave;
-  const int64_t row = qw + l32;
+  int64_t b, g, qrow;                             // qrow: the lane's row in [B, Hq, Nq] order
+  int64_t NK;                                     // key rows per KV head in memory
+  // last visible key of the lane's row, of the wave's first and last rows, of the workgroup's
+  // last row (-1: none); rows are ordered so that these limits never decrease along the rows
+  int lim, lim_lo, lim_hi, lim_wg;
+  int klen;                                       // valid keys (cache forward)
+  bool valid = true;                              // the lane's row exists (cache forward)
+  if constexpr (KV) {
+    b = bh / p.Hkv;
+    g = bh - b * p.Hkv;
+    NK = p.Nk;
+    const int64_t RK = p.Nq * G;                  // packed rows of this KV head
+    const int64_t pr0 = qt * 32 * W, prw = pr0 + 32 * wave, pr = prw + l32;
+    valid = pr < RK;
+    const int64_t prc = min(pr, RK - 1);
+    const int64_t i = prc / G;
+    qrow = (b * p.Hq + g * G + (prc - i * G)) * p.Nq + i;
+    const int64_t len = p.seqlens != nullptr ? min(max((int64_t)p.seqlens[b], (int64_t)0), p.Nk) : p.Nk;
+    klen = (int)len;
+    auto lim_of = [&](int64_t r) -> int { return (int)(CAUSAL ? min(len - p.Nq + r / G, len - 1) : len - 1); };
+    lim = valid ? lim_of(prc) : -1;
+    lim_lo = prw < RK ? lim_of(prw) : -1;
+    lim_hi = prw < RK ? lim_of(min(prw + 31, RK - 1)) : -1;
+    lim_wg = lim_of(min(pr0 + 32 * W - 1, RK - 1));
+  } else {
+    b = bh / p.Hq;
+    const int64_t h = bh - b * p.Hq;
+    g = h / G;
+    NK = p.N;
+    const int64_t q0 = qt * 32 * W, qw = q0 + 32 * wave, row = qw + l32;
+    qrow = (b * p.Hq + h) * p.N + row;
+    lim = (int)(CAUSAL ? row : p.N - 1);
+    lim_lo = (int)(CAUSAL ? qw : p.N - 1);
+    lim_hi = (int)(CAUSAL ? qw + 31 : p.N - 1);
+    lim_wg = (int)(CAUSAL ? q0 + 32 * W - 1 : p.N - 1);
+    klen = (int)p.N;
+  }
 
   // K^ / V^ of this KV head as buffer resources: 32-bit lane offsets, the tile offset in an SGPR
   const int64_t kvh = b * p.Hkv + g;
-  const auto kc_rs = make_rsrc(p.k_codes + kvh * N * (D / 2), N * (D / 2));
-  const auto ks_rs = make_rsrc(p.k_scales + kvh * N * (D / 32), N * (D / 32));
-  const auto vc_rs = make_rsrc(p.v_codes + kvh * D * (N / 2), D * (N / 2));
-  const auto vs_rs = make_rsrc(p.v_scales + kvh * D * (N / 32), D * (N / 32));
+  const auto kc_rs = make_rsrc(p.k_codes + kvh * NK * (D / 2), NK * (D / 2));
+  const auto ks_rs = make_rsrc(p.k_scales + kvh * NK * (D / 32), NK * (D / 32));
+  const auto vc_rs = make_rsrc(p.v_codes + kvh * D * (NK / 2), D * (NK / 2));
+  const auto vs_rs = make_rsrc(p.v_scales + kvh * D * (NK / 32), D * (NK / 32));
 
   // ---- the wave's Q^ as the B operand of S^T = K^ Q^T (fixed for the whole kernel) ----
   v4i qb[KS_STEPS];
   int qsc;
   {
-    const uint8_t* qr = p.q_codes + ((b * p.Hq + h) * N + row) * (D / 2);
+    const uint8_t* qr = p.q_codes + qrow * (D / 2);
 #pragma unroll
     for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks);
-    const uint8_t* qs = p.q_scales + ((b * p.Hq + h) * N + row) * (D / 32);
+    const uint8_t* qs = p.q_scales + qrow * (D / 32);
     qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 16)) : (int)qs[hi];
   }
 
@@ -239,8 +277,8 @@ fwd_kernel(FwdParams p) {
                                                                ksc, 2, qsc);
       }
     }
-    if (CAUSAL && ((int64_t)t * BC + BC - 1 > qw)) {   // diagonal tile: key j > row i -> -inf
-      const int jrel = (int)(row - (int64_t)t * BC) - 32 * hi;   // register r of T holds key 32 hi + 16T + r
+    if ((CAUSAL || KV) && t * BC + BC - 1 > lim_lo) {   // keys past a row's limit -> -inf
+      const int jrel = lim - t * BC - 32 * hi;        // register r of T holds key 32 hi + 16T + r
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
@@ -257,16 +295,18 @@ fwd_kernel(FwdParams p) {
     const float bm = fmaxf(a, sT[1][15]);
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     const float m_new = fmaxf(m_run, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    // a row that has seen no key yet keeps m = -inf; its shift is taken as 0 (alpha = 0, p = 0)
+    const float m_sh = KV ? (m_new == -__builtin_inff() ? 0.0f : m_new) : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_sh) * c);
     m_run = m_new;
     // E8M0 scale of the block from its max p = exp2((bm - m) c): the biased exponent of p is
     // floor((bm - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
     // that - 2, clamped below at 1 (affects only P < 2^-124; a fully masked block gives -inf).
-    const int psc = (int)fmaxf(__builtin_floorf((bm - m_new) * c), -124.0f) + 125;
+    const int psc = (int)fmaxf(__builtin_floorf((bm - m_sh) * c), -124.0f) + 125;
     const float sc = __uint_as_float((uint32_t)psc << 23);
     // p = exp2(s c - m c) and E2M1 conversion against the block scale; the packed codes are
     // already the B operand of the PV MFMA (lane l: keys 32(l/32) .. +31 of query l%32)
-    const float mc = m_new * c;
+    const float mc = m_sh * c;
     uint32_t pk[2][2];
     if constexpr (EFQ) {
       // exp-free codes: k = clamp(rne(A y + B), 0, 7) with y = x - e, x = s c - m c = log2 p and
@@ -322,14 +362,15 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const v8i va = widen(*reinterpret_cast<const v4i*>(base + vr_off + ct * 32 * 32));
-      const int vsc = base[vsr_off + 32 * ct];
+      int vsc = base[vsr_off + 32 * ct];
+      if constexpr (KV) vsc = t * BC + 32 * hi >= klen ? 127 : vsc;   // block wholly past the length
       o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], 4, 4, 0, vsc, 0, psc);
     }
   };
 
   // ---- tile loop: unrolled over the stages so that stage offsets are static ----
-  const int ntiles = (int)(CAUSAL ? ((q0 + 32 * W - 1) / BC + 1) : (N / BC));
-  const int last_active = CAUSAL ? (int)((qw + 31) / BC) : ntiles - 1;   // wave-uniform
+  const int ntiles = lim_wg >= 0 ? lim_wg / BC + 1 : 0;                 // workgroup-uniform
+  const int last_active = lim_hi >= 0 ? lim_hi / BC : -1;                // wave-uniform
 
   // The barrier that ends step t publishes tile t + 1: each wave first waits for its own DMAs up
   // to that tile's (all but the JPW issued by each later step), and for its LDS reads (the stage
@@ -368,8 +409,9 @@ fwd_kernel(FwdParams p) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum[0]), __float_as_uint(lsum[1]), false, false);
   auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[0], false, false);
   const float lrow = __uint_as_float(r32[0]);
-  const float inv = 1.0f / lrow;
-  uint16_t* orow = p.o + ((b * p.Hq + h) * N + row) * D;
+  const float inv = KV ? (lrow > 0.0f ? 1.0f / lrow : 0.0f) : 1.0f / lrow;
+  if (!valid) return;
+  uint16_t* orow = p.o + qrow * D;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -381,30 +423,42 @@ fwd_kernel(FwdParams p) {
       *reinterpret_cast<uint2*>(orow + ch) = w;
     }
   if (hi == 0) {
-    p.m[(b * p.Hq + h) * N + row] = m_run * p.scale_nat;
-    p.l[(b * p.Hq + h) * N + row] = lrow;
+    p.m[qrow] = m_run * p.scale_nat;
+    p.l[qrow] = lrow;
   }
 }
 
-template <int D, int W, bool CAUSAL, bool EFQ>
+template <int D, int W, bool CAUSAL, bool EFQ, bool KV>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const int64_t blocks = (p.N / (32 * W)) * p.Hq * p.B;
-  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL, EFQ>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  const int64_t blocks = KV ? ((p.Nq * (p.Hq / p.Hkv) + 32 * W - 1) / (32 * W)) * p.Hkv * p.B
+                            : (p.N / (32 * W)) * p.Hq * p.B;
+  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL, EFQ, KV>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool EFQ>
+template <int D, bool EFQ, bool KV>
 hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
-  // four waves (128 rows) per workgroup when the rows tile evenly, else two (N % 64 == 0)
-  if (p.N % 128 == 0) return causal ? launch<D, 4, true, EFQ>(p, stream) : launch<D, 4, false, EFQ>(p, stream);
-  return causal ? launch<D, 2, true, EFQ>(p, stream) : launch<D, 2, false, EFQ>(p, stream);
+  // four waves (128 rows) per workgroup when the rows tile evenly (plain forward) or there are
+  // enough of them (cache forward), else two
+  const bool w4 = KV ? p.Nq * (p.Hq / p.Hkv) >= 256 : p.N % 128 == 0;
+  if (w4) return causal ? launch<D, 4, true, EFQ, KV>(p, stream) : launch<D, 4, false, EFQ, KV>(p, stream);
+  return causal ? launch<D, 2, true, EFQ, KV>(p, stream) : launch<D, 2, false, EFQ, KV>(p, stream);
+}
+
+template <bool KV>
+hipError_t launch_any(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream) {
+  if (efq) return d == 128 ? launch_d<128, true, KV>(p, causal, stream) : launch_d<64, true, KV>(p, causal, stream);
+  return d == 128 ? launch_d<128, false, KV>(p, causal, stream) : launch_d<64, false, KV>(p, causal, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream) {
-  if (efq) return d == 128 ? launch_d<128, true>(p, causal, stream) : launch_d<64, true>(p, causal, stream);
-  return d == 128 ? launch_d<128, false>(p, causal, stream) : launch_d<64, false>(p, causal, stream);
+  return launch_any<false>(p, d, causal, efq, stream);
+}
+
+hipError_t launch_fwd_kvcache(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream) {
+  return launch_any<true>(p, d, causal, efq, stream);
 }
 
 }  // namespace attnfp4

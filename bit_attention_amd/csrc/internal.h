@@ -19,6 +19,10 @@ struct FwdParams {
   int64_t B, Hq, Hkv, N;
   float c;          // softmax_scale * log2(e): raw score -> base-2 exponent
   float scale_nat;  // softmax_scale: raw score -> natural-log units (saved m)
+  // cache forward only: Nq new query rows per head, a key/value cache of capacity Nk per KV
+  // head and per-sequence valid lengths (null: every sequence has Nk)
+  int64_t Nq, Nk;
+  const int32_t* seqlens;
 };
 
 struct BwdParams {
@@ -58,6 +62,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
                            void* scales, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
+hipError_t launch_fwd_kvcache(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace attnfp4

@@ -29,6 +29,7 @@ EXPORTED = (
     "attn_fp4_status_string",
     "attn_fp4_quantize",
     "attn_fp4_fwd",
+    "attn_fp4_fwd_kvcache",
     "attn_fp4_bwd_workspace_bytes",
     "attn_fp4_bwd_recompute",
 )
@@ -54,6 +55,20 @@ class FwdArgs(ctypes.Structure):
 
 
 P_EXP, P_EFQ = 0, 1   # P~ rules of the forward (exp-then-quantize; exp-free EFQ codes)
+
+
+class FwdKvcacheArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_codes", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("seqlens_k", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("p_rule", ctypes.c_int32),
+    ]
 
 
 class BwdArgs(ctypes.Structure):
@@ -89,6 +104,8 @@ def lib():
                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.attn_fp4_fwd.restype = ctypes.c_int32
         L.attn_fp4_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.attn_fp4_fwd_kvcache.restype = ctypes.c_int32
+        L.attn_fp4_fwd_kvcache.argtypes = [ctypes.POINTER(FwdKvcacheArgs), ctypes.c_void_p]
         L.attn_fp4_bwd_workspace_bytes.restype = ctypes.c_int64
         L.attn_fp4_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 5
         L.attn_fp4_bwd_recompute.restype = ctypes.c_int32
@@ -179,6 +196,45 @@ def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal
     a = FwdArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
                 _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale), int(p_rule))
     _check(lib().attn_fp4_fwd(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd")
+    return o, m, l
+
+
+def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k=None,
+                         causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP):
+    """Forward of Nq new query rows against a pre-quantized key/value cache of capacity Nk.
+
+    q_codes [B, Hq, Nq, d/2]; k_codes [B, Hkv, Nk, d/2]; v_codes [B, Hkv, Nk/32, d, 16] (the cache
+    quantized as a whole); seqlens_k: int32 device tensor [B] of valid cache lengths, or None for
+    Nk.  The new rows are the last Nq positions of each sequence (bottom-right causal alignment).
+    Returns (o bf16 [B, Hq, Nq, d], m fp32 [B, Hq, Nq], l fp32 [B, Hq, Nq]).
+    """
+    B, Hq, Nq, dh = q_codes.shape
+    d = 2 * dh
+    Hkv, Nk = k_codes.shape[1], k_codes.shape[2]
+    for t, name in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
+                    (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, torch.uint8, name)
+    if k_codes.shape != (B, Hkv, Nk, dh) or v_codes.shape != (B, Hkv, Nk // 32, d, 16):
+        raise ValueError("inconsistent operand shapes")
+    if q_scales.shape != (B, Hq, Nq, d // 32) or k_scales.shape != (B, Hkv, Nk, d // 32) \
+            or v_scales.shape != (B, Hkv, Nk // 32, d):
+        raise ValueError("inconsistent scale shapes")
+    if seqlens_k is not None:
+        _dev(seqlens_k, torch.int32, "seqlens_k")
+        if seqlens_k.shape != (B,):
+            raise ValueError("seqlens_k must be [B]")
+    dev = q_codes.device
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+    if m is None:
+        m = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    a = FwdKvcacheArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                       _ptr(v_scales), None if seqlens_k is None else _ptr(seqlens_k),
+                       _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                       float(softmax_scale), int(p_rule))
+    _check(lib().attn_fp4_fwd_kvcache(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd_kvcache")
     return o, m, l
 
 

@@ -134,3 +134,64 @@ def sample_rows(N, count=512, seed=BASE_SEED, edge=64):
     r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, N, 77])))
     extra = r.choice(pool, size=max(0, count - fixed.shape[0]), replace=False)
     return np.sort(np.concatenate([fixed, extra]))
+
+
+# ---- cache forward workloads: Nq new rows against a key/value cache of capacity Nk -------------
+@dataclass(frozen=True)
+class CacheWorkload:
+    name: str
+    wid: int
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    kind: str                      # distribution recipe, as for Workload
+    len_lo: int                    # valid cache lengths are drawn uniformly in [len_lo, Nk]
+    note: str = field(default="", compare=False)
+
+
+CACHE_WORKLOADS = {
+    w.name: w
+    for w in [
+        CacheWorkload("decode_b8hq32hkv8nk32768d128", 5, 8, 32, 8, 1, 32768, 128, True, "llm_outlier", 8192,
+                      note="one new token per sequence; cache lengths U[8192, 32768]; LLM value mix"),
+        CacheWorkload("prefill_chunk_b1hq32hkv8nq2048nk32768d128", 6, 1, 32, 8, 2048, 32768, 128, True,
+                      "gqa_outlier", 32768,
+                      note="the last 2048-token chunk of a 32768-token prompt, causal"),
+    ]
+}
+
+
+def gen_cache_head(w, tensor, b, h, seed=BASE_SEED):
+    """One head of a cache workload: 'q' [Nq, d], or 'k' / 'v' [Nk, d] (the whole capacity)."""
+    if isinstance(w, str):
+        w = CACHE_WORKLOADS[w]
+    nh = w.Hq if tensor == "q" else w.Hkv
+    if not (0 <= b < w.B and 0 <= h < nh):
+        raise IndexError("head (%d, %d) out of range for %s" % (b, h, tensor))
+    n = w.Nq if tensor == "q" else w.Nk
+    shape = Workload(w.name, w.wid, w.B, w.Hq, w.Hkv, n, w.d, w.causal, w.kind)
+    return _draw_head(shape, tensor, b, h, seed)
+
+
+def gen_cache_tensor(w, tensor, seed=BASE_SEED):
+    """Whole tensor of a cache workload: q [B, Hq, Nq, d] or k / v [B, Hkv, Nk, d]."""
+    if isinstance(w, str):
+        w = CACHE_WORKLOADS[w]
+    nh, n = (w.Hq, w.Nq) if tensor == "q" else (w.Hkv, w.Nk)
+    out = np.empty((w.B, nh, n, w.d), dtype=np.float32)
+    for b in range(w.B):
+        for h in range(nh):
+            out[b, h] = gen_cache_head(w, tensor, b, h, seed)
+    return out
+
+
+def cache_lengths(w, seed=BASE_SEED):
+    """Valid cache lengths [B] (int32), seeded, uniform in [len_lo, Nk]."""
+    if isinstance(w, str):
+        w = CACHE_WORKLOADS[w]
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, w.wid, 101])))
+    return r.integers(w.len_lo, w.Nk, size=w.B, endpoint=True).astype(np.int32)

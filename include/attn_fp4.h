@@ -145,6 +145,51 @@ enum { ATTN_FP4_P_EXP = 0, ATTN_FP4_P_EFQ = 1 };
 int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
 
 /*
+ * Cache forward arguments (FP4 attention for LLM inference, Attn-QAT
+ * abstract: new query rows attend to keys and values that were quantized
+ * once and are kept; chunked prefill and decode).
+ *   q_codes   [B, Hq, Nq, d/2]   q_scales [B, Hq, Nq, d/32]  (axis 0)
+ *   k_codes   [B, Hkv, Nk, d/2]  k_scales [B, Hkv, Nk, d/32] (axis 0)
+ *   v_codes   [B, Hkv, Nk/32, d, 16]  v_scales [B, Hkv, Nk/32, d]
+ *             (axis 1 over the cache's whole capacity Nk, block-major)
+ *   seqlens_k int32 [B] device array: valid cache length L_b of sequence
+ *             b (values are clamped to [0, Nk]); NULL means L_b = Nk.
+ *   o bf16 [B, Hq, Nq, d]; m, l fp32 [B, Hq, Nq] (outputs, as attn_fp4_fwd)
+ * The Nq new rows are the last Nq positions of each sequence: their keys
+ * and values are already in the cache, and new row i sits at position
+ * L_b - Nq + i.  Keys j < L_b are visible; with causal != 0 only those with
+ * j <= L_b - Nq + i (bottom-right alignment).  A row that sees no key
+ * (L_b = 0, or causal with L_b - Nq + i < 0) gets O = 0, m = -inf, l = 0.
+ * Cache memory past L_b is read only inside the last 64-key tile and never
+ * changes the result, except that the scale of a V^ block that holds both
+ * valid and later positions is the one stored (the cache quantized as a
+ * whole).  Key tiles are visited in ascending order and P~ is requantized
+ * per 32-key block exactly as in attn_fp4_fwd, so with Nq = Nk = L_b this is
+ * attn_fp4_fwd.  p_rule as for attn_fp4_fwd.
+ * Supported: d == 128 or d == 64, Nq >= 1, Nk % 64 == 0, Hq % Hkv == 0.
+ * Errors: ATTN_FP4_E_INVALID_ARG (null/misaligned pointer, bad dims or
+ * enum), ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP.
+ */
+typedef struct {
+  const void* q_codes;
+  const void* q_scales;
+  const void* k_codes;
+  const void* k_scales;
+  const void* v_codes;
+  const void* v_scales;
+  const int32_t* seqlens_k;
+  void* o;
+  float* m;
+  float* l;
+  int64_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t causal;
+  float softmax_scale;
+  int32_t p_rule;
+} attn_fp4_fwd_kvcache_args;
+
+int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* args, void* stream);
+
+/*
  * Backward arguments.  Quantized operands as for the forward; o, m, l are
  * the forward's outputs; do_ is bf16 [B, Hq, N, d].  Outputs dq bf16
  * [B, Hq, N, d], dk and dv bf16 [B, Hkv, N, d] (summed over the query heads

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert ops.attn_fp4_abi_version() == 3
+    assert ops.attn_fp4_abi_version() == 4
 
 
 def test_status_strings():
@@ -56,6 +56,14 @@ def test_host_validation_rejects_before_launch():
         dims.update(kw)
         a = ops.FwdArgs(p, p, p, p, p, p, p, p, p, dims["B"], dims["Hq"], dims["Hkv"], dims["N"], dims["d"], 0, 0.0)
         assert L.attn_fp4_fwd(ctypes.byref(a), None) == 1, kw
+    # cache forward: capacity not a multiple of 64, Nq = 0, bad group, bad d, misaligned lengths
+    assert L.attn_fp4_fwd_kvcache(None, None) == 1
+    for kw in ({"Nk": 96}, {"Nq": 0}, {"Hkv": 3}, {"d": 96}, {"seq": ctypes.c_void_p(258)}, {"p_rule": 2}):
+        dims = dict(B=1, Hq=4, Hkv=2, Nq=1, Nk=128, d=128, seq=None, p_rule=0)
+        dims.update(kw)
+        a = ops.FwdKvcacheArgs(p, p, p, p, p, p, dims["seq"], p, p, p, dims["B"], dims["Hq"], dims["Hkv"],
+                               dims["Nq"], dims["Nk"], dims["d"], 0, 0.0, dims["p_rule"])
+        assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 1, kw
     # rows: 3 x [B*Hq*N] fp32; bf16 copies: V^ and K^T per KV head, Q^T and dO^T per query head
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 3 * 1024 + 4 * (2 * 128 * 128 * 2)
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -100,6 +100,9 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
   p.Nq = a->N;
   p.Nk = a->N;
   p.seqlens = nullptr;
+  p.splits = 1;
+  p.tps = a->N / 64;
+  p.ws_smax = p.ws_m = p.ws_l = p.ws_o = nullptr;
   const double s = resolve_scale(a->softmax_scale, a->d);
   p.c = (float)(s * 1.4426950408889634);
   p.scale_nat = (float)s;
@@ -107,15 +110,26 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
   return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
 }
 
+static int32_t check_kvcache_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return ATTN_FP4_E_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_FP4_E_INVALID_ARG;
+  if (Nk % 64 != 0 || Hq % Hkv != 0) return ATTN_FP4_E_INVALID_ARG;
+  // 32-bit buffer offsets within one KV head's cache, and the grid: at most one workgroup per
+  // 64 packed query rows (times the splits)
+  if (Nk * d > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  if ((Nq * (Hq / Hkv) + 63) / 64 * Hkv * B * (Nk / 64) > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  return ATTN_FP4_OK;
+}
+
+int64_t attn_fp4_fwd_kvcache_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  if (check_kvcache_dims(B, Hq, Hkv, Nq, Nk, d) != ATTN_FP4_OK) return -1;
+  return attnfp4::kv_split_plan(B, Hq, Hkv, Nq, Nk, d).total;
+}
+
 int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
-  if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Nq <= 0 || a->Nk <= 0) return ATTN_FP4_E_INVALID_ARG;
-  if (a->d != 64 && a->d != 128) return ATTN_FP4_E_INVALID_ARG;
-  if (a->Nk % 64 != 0 || a->Hq % a->Hkv != 0) return ATTN_FP4_E_INVALID_ARG;
-  // 32-bit buffer offsets within one KV head's cache, and the grid: at most one workgroup per
-  // 64 packed query rows
-  if (a->Nk * a->d > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
-  if ((a->Nq * (a->Hq / a->Hkv) + 63) / 64 * a->Hkv * a->B > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st0 = check_kvcache_dims(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
+  if (st0 != ATTN_FP4_OK) return st0;
   const void* ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes,
                         a->v_scales, a->o, a->m, a->l};
   for (const void* ptr : ptrs)
@@ -123,6 +137,10 @@ int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   if (a->seqlens_k != nullptr && (reinterpret_cast<uintptr_t>(a->seqlens_k) & 3u) != 0) return ATTN_FP4_E_INVALID_ARG;
   if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
   if (a->p_rule != ATTN_FP4_P_EXP && a->p_rule != ATTN_FP4_P_EFQ) return ATTN_FP4_E_INVALID_ARG;
+  const attnfp4::KvSplit ks = attnfp4::kv_split_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
+  if (a->workspace != nullptr && ks.splits > 1 &&
+      ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 || a->workspace_bytes < ks.total))
+    return ATTN_FP4_E_WORKSPACE;
   int32_t st = check_device();
   if (st != ATTN_FP4_OK) return st;
   attnfp4::FwdParams p;
@@ -142,6 +160,18 @@ int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   p.Nq = a->Nq;
   p.Nk = a->Nk;
   p.seqlens = a->seqlens_k;
+  p.splits = 1;
+  p.tps = a->Nk / 64;
+  p.ws_smax = p.ws_m = p.ws_l = p.ws_o = nullptr;
+  if (a->workspace != nullptr && ks.splits > 1) {
+    uint8_t* w = (uint8_t*)a->workspace;
+    p.splits = ks.splits;
+    p.tps = ks.tps;
+    p.ws_smax = (float*)(w + ks.smax);
+    p.ws_m = (float*)(w + ks.m);
+    p.ws_l = (float*)(w + ks.l);
+    p.ws_o = (float*)(w + ks.o);
+  }
   const double s = resolve_scale(a->softmax_scale, a->d);
   p.c = (float)(s * 1.4426950408889634);
   p.scale_nat = (float)s;

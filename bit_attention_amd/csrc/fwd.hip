@@ -78,7 +78,12 @@ constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
 // one pass over the cache serves the whole group.  Rows that see no key give O = 0, m = -inf,
 // l = 0; V^ blocks wholly past L_b take a unit scale, so that cache memory past the length,
 // whatever it holds, cannot turn the zero P~ of the masked keys into NaN.
-template <int D, int W, bool CAUSAL, bool EFQ, bool KV>
+// SPLIT (with KV) runs one range of `tps` key tiles per workgroup: the running max starts at the
+// largest score of the earlier ranges (from kv_max_kernel), which is exactly the running max the
+// sequential loop would carry into the range, so every P~ code is the sequential one; the
+// range's running max, row sum and unnormalised accumulator go to the workspace for
+// kv_merge_kernel.
+template <int D, int W, bool CAUSAL, bool EFQ, bool KV, bool SPLIT>
 __global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W>(), waves_per_simd<D, W>())))
 fwd_kernel(FwdParams p) {
@@ -105,12 +110,15 @@ fwd_kernel(FwdParams p) {
   // ---- work item: XCD-aware remap so that the workgroups of one head run on one XCD ----
   const int64_t G = p.Hq / p.Hkv;                 // query heads per KV head
   const int64_t nqt = KV ? (p.Nq * G + 32 * W - 1) / (32 * W) : p.N / (32 * W);
-  const int64_t total = nqt * (KV ? p.Hkv : p.Hq) * p.B;
+  const int64_t nsp = SPLIT ? p.splits : 1;
+  const int64_t total = nqt * (KV ? p.Hkv : p.Hq) * p.B * nsp;
   int64_t id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const int64_t sp = SPLIT ? id % nsp : 0;        // key-tile range (split forward)
+  id = SPLIT ? id / nsp : id;
   const int64_t bh = id / nqt;                    // (b, query head), cache forward: (b, KV head)
   int64_t qt = id - bh * nqt;
-  if (CAUSAL) qt = nqt - 1 - qt;                  // longest rows first
+  if (CAUSAL && !SPLIT) qt = nqt - 1 - qt;        // longest rows first
   int64_t b, g, qrow;                             // qrow: the lane's row in [B, Hq, Nq] order
   int64_t NK;                                     // key rows per KV head in memory
   // last visible key of the lane's row, of the wave's first and last rows, of the workgroup's
@@ -118,6 +126,7 @@ fwd_kernel(FwdParams p) {
   int lim, lim_lo, lim_hi, lim_wg;
   int klen;                                       // valid keys (cache forward)
   bool valid = true;                              // the lane's row exists (cache forward)
+  int64_t prow = 0;                               // the lane's packed row (cache forward)
   if constexpr (KV) {
     b = bh / p.Hkv;
     g = bh - b * p.Hkv;
@@ -125,6 +134,7 @@ fwd_kernel(FwdParams p) {
     const int64_t RK = p.Nq * G;                  // packed rows of this KV head
     const int64_t pr0 = qt * 32 * W, prw = pr0 + 32 * wave, pr = prw + l32;
     valid = pr < RK;
+    prow = pr;
     const int64_t prc = min(pr, RK - 1);
     const int64_t i = prc / G;
     qrow = (b * p.Hq + g * G + (prc - i * G)) * p.Nq + i;
@@ -259,6 +269,11 @@ fwd_kernel(FwdParams p) {
   for (int ct = 0; ct < CT; ++ct) o[ct] = v16f{};
   v4f lsum = v4f{};
   float m_run = -__builtin_inff();
+  const int64_t RKs = SPLIT ? p.Nq * G : 0;       // packed rows per KV head (workspace rows)
+  if constexpr (SPLIT) {                          // the running max carried into this range
+    if (valid)
+      for (int64_t s2 = 0; s2 < sp; ++s2) m_run = fmaxf(m_run, p.ws_smax[(bh * nsp + s2) * RKs + prow]);
+  }
   const float c = p.c;
 
   // ---- one 64-key tile: S^T, online softmax, P~ requantization, row sums and PV ----
@@ -369,7 +384,10 @@ fwd_kernel(FwdParams p) {
   };
 
   // ---- tile loop: unrolled over the stages so that stage offsets are static ----
-  const int ntiles = lim_wg >= 0 ? lim_wg / BC + 1 : 0;                 // workgroup-uniform
+  const int ntl_all = lim_wg >= 0 ? lim_wg / BC + 1 : 0;                // workgroup-uniform
+  const int tb = SPLIT ? (int)(sp * p.tps) : 0;                          // first tile of the range
+  const int ntiles = SPLIT ? min((int)p.tps, ntl_all - tb) : ntl_all;    // tiles in the range
+  if (SPLIT && ntiles <= 0) return;                                      // whole workgroup
   const int last_active = lim_hi >= 0 ? lim_hi / BC : -1;                // wave-uniform
 
   // The barrier that ends step t publishes tile t + 1: each wave first waits for its own DMAs up
@@ -377,14 +395,14 @@ fwd_kernel(FwdParams p) {
   // of tile t is refilled in step t + 1).  The asm statements also keep the compiler from moving
   // memory accesses across the barrier.
   for (int k = 0; k < PD; ++k)
-    if (k < ntiles) issue_tile(k, smem + k * S::BYTES);
+    if (k < ntiles) issue_tile(tb + k, smem + k * S::BYTES);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   static_assert(2 * JPW <= 15, "vmcnt immediate");
   auto step = [&](int t, auto stc) {
     constexpr int st = decltype(stc)::value;
-    if (t + PD < ntiles) issue_tile(t + PD, smem + ((st + PD) % NSTAGE) * S::BYTES);
-    if (t <= last_active) tile(t, smem + st * S::BYTES);
+    if (t + PD < ntiles) issue_tile(tb + t + PD, smem + ((st + PD) % NSTAGE) * S::BYTES);
+    if (tb + t <= last_active) tile(tb + t, smem + st * S::BYTES);
     const int newer = min(max(ntiles - t - 2, 0), PD - 1);   // later steps that issued DMAs
     if (PD > 2 && newer >= 2)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * JPW) : "memory");
@@ -409,6 +427,22 @@ fwd_kernel(FwdParams p) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum[0]), __float_as_uint(lsum[1]), false, false);
   auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[0], false, false);
   const float lrow = __uint_as_float(r32[0]);
+  if constexpr (SPLIT) {                          // the range's partial results
+    if (!valid) return;
+    const int64_t wr = (bh * nsp + sp) * RKs + prow;
+    float* orow = p.ws_o + wr * D;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * a + 4 * hi) =
+            make_float4(o[ct][4 * a], o[ct][4 * a + 1], o[ct][4 * a + 2], o[ct][4 * a + 3]);
+    if (hi == 0) {
+      p.ws_m[wr] = m_run;
+      p.ws_l[wr] = lrow;
+    }
+    return;
+  }
   const float inv = KV ? (lrow > 0.0f ? 1.0f / lrow : 0.0f) : 1.0f / lrow;
   if (!valid) return;
   uint16_t* orow = p.o + qrow * D;
@@ -428,11 +462,140 @@ fwd_kernel(FwdParams p) {
   }
 }
 
+// ---- split cache forward, pass 1: the largest visible raw score per (split, packed row) ----
+// Workgroups of two waves take 64 packed rows and one range of key tiles, as the split forward
+// does; K^ is read straight into the MFMA A operand (no LDS, keys in natural order: the maximum
+// does not depend on where a key sits) and the scores are the forward's, bit for bit (same
+// operands, scales and k-step order).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
+  constexpr int KS_STEPS = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int64_t G = p.Hq / p.Hkv, RK = p.Nq * G, nqt = (RK + 63) / 64, nsp = p.splits;
+  int64_t id = blockIdx.x;
+  const int64_t sp = id % nsp;
+  id /= nsp;
+  const int64_t bh = id / nqt, qt = id - bh * nqt;
+  const int64_t b = bh / p.Hkv, g = bh - b * p.Hkv;
+  const int64_t pr0 = qt * 64, prw = pr0 + 32 * wave, pr = prw + l32;
+  const bool valid = pr < RK;
+  const int64_t prc = min(pr, RK - 1);
+  const int64_t i = prc / G;
+  const int64_t qrow = (b * p.Hq + g * G + (prc - i * G)) * p.Nq + i;
+  const int64_t len = p.seqlens != nullptr ? min(max((int64_t)p.seqlens[b], (int64_t)0), p.Nk) : p.Nk;
+  auto lim_of = [&](int64_t r) -> int { return (int)(CAUSAL ? min(len - p.Nq + r / G, len - 1) : len - 1); };
+  const int lim = valid ? lim_of(prc) : -1;
+  const int lim_lo = prw < RK ? lim_of(prw) : -1;
+  const int lim_hi = prw < RK ? lim_of(min(prw + 31, RK - 1)) : -1;
+  const int lim_wg = lim_of(min(pr0 + 63, RK - 1));
+  const int ntl_all = lim_wg >= 0 ? lim_wg / 64 + 1 : 0;
+  const int tb = (int)(sp * p.tps);
+  const int te = min(tb + (int)p.tps, min(ntl_all, lim_hi >= 0 ? lim_hi / 64 + 1 : 0));
+  float mx = -__builtin_inff();
+  if (tb < te) {
+    v4i qb[KS_STEPS];
+    const uint8_t* qr = p.q_codes + qrow * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS_STEPS; ++ks) qb[ks] = *reinterpret_cast<const v4i*>(qr + 16 * hi + 32 * ks);
+    const uint8_t* qs = p.q_scales + qrow * (D / 32);
+    const int qsc = (D == 128) ? (int)(qs[hi] | (qs[2 + hi] << 16)) : (int)qs[hi];
+    const int64_t kvh = b * p.Hkv + g;
+    const auto kc_rs = make_rsrc(p.k_codes + kvh * p.Nk * (D / 2), p.Nk * (D / 2));
+    const auto ks_rs = make_rsrc(p.k_scales + kvh * p.Nk * (D / 32), p.Nk * (D / 32));
+    for (int t = tb; t < te; ++t) {
+      const int tt = __builtin_amdgcn_readfirstlane(t);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int key = 32 * T + l32;             // A row l32 of half T: key 64 t + 32 T + l32
+        v16f acc;
+        int ksc;
+        if constexpr (D == 128)
+          ksc = (int)((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ks_rs, 4 * key, tt * 256, 0) >> (8 * hi));
+        else
+          ksc = (int)__builtin_amdgcn_raw_buffer_load_b8(ks_rs, 2 * key + hi, tt * 128, 0);
+        const v4i ka0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kc_rs, key * (D / 2) + 16 * hi, tt * (64 * D / 2), 0));
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
+        if constexpr (KS_STEPS == 2) {
+          const v4i ka1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kc_rs, key * (D / 2) + 32 + 16 * hi, tt * (64 * D / 2), 0));
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka1), widen(qb[1]), acc, 4, 4, 2, ksc, 2, qsc);
+        }
+        // register r holds key 64 t + 32 T + 8 (r / 4) + 4 hi + r % 4 of query l32
+        if (t * 64 + 63 > lim_lo) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t * 64 + 32 * T + 8 * (r >> 2) + 4 * hi + (r & 3) > lim) acc[r] = -__builtin_inff();
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      }
+    }
+  }
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  if (valid && hi == 0) p.ws_smax[(bh * nsp + sp) * RK + pr] = mx;
+}
+
+// ---- split cache forward, pass 3: merge the ranges' partial results into O, m, l ----
+// One wave per packed row.  With M the largest running max over the ranges, range s contributes
+// exp2((m_s - M) c) times its accumulator and row sum: the sequential loop's history rescaling
+// written as one factor per range.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) kv_merge_kernel(FwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t G = p.Hq / p.Hkv, RK = p.Nq * G, nsp = p.splits;
+  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rid >= p.B * p.Hkv * RK) return;
+  const int64_t bh = rid / RK, pr = rid - bh * RK;
+  const int64_t b = bh / p.Hkv, g = bh - b * p.Hkv;
+  const int64_t i = pr / G;
+  const int64_t qrow = (b * p.Hq + g * G + (pr - i * G)) * p.Nq + i;
+  // the ranges the split forward ran for this row's workgroup (64 packed rows)
+  const int64_t len = p.seqlens != nullptr ? min(max((int64_t)p.seqlens[b], (int64_t)0), p.Nk) : p.Nk;
+  const int64_t last = min((pr / 64) * 64 + 63, RK - 1);
+  const int64_t lim_wg = CAUSAL ? min(len - p.Nq + last / G, len - 1) : len - 1;
+  const int64_t nr = lim_wg >= 0 ? (lim_wg / 64) / p.tps + 1 : 0;
+  float M = -__builtin_inff();
+  for (int64_t s = 0; s < nr; ++s) M = fmaxf(M, p.ws_m[(bh * nsp + s) * RK + pr]);
+  constexpr int CPL = D / 64;                       // channels per lane
+  float acc[CPL] = {};
+  float lt = 0.0f;
+  if (M != -__builtin_inff()) {
+    for (int64_t s = 0; s < nr; ++s) {
+      const int64_t wr = (bh * nsp + s) * RK + pr;
+      const float w = __builtin_amdgcn_exp2f((p.ws_m[wr] - M) * p.c);
+      lt += w * p.ws_l[wr];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] += w * p.ws_o[wr * D + CPL * lane + k];
+    }
+  }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* orow = p.o + qrow * D + CPL * lane;
+  if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(orow) = pk_bf16(acc[0] * inv, acc[1] * inv);
+  else orow[0] = (uint16_t)(pk_bf16(acc[0] * inv, 0.0f) & 0xFFFFu);
+  if (lane == 0) {
+    p.m[qrow] = M * p.scale_nat;
+    p.l[qrow] = lt;
+  }
+}
+
 template <int D, int W, bool CAUSAL, bool EFQ, bool KV>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t blocks = KV ? ((p.Nq * (p.Hq / p.Hkv) + 32 * W - 1) / (32 * W)) * p.Hkv * p.B
                             : (p.N / (32 * W)) * p.Hq * p.B;
-  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL, EFQ, KV>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, W, CAUSAL, EFQ, KV, false>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool EFQ>
+hipError_t launch_split(const FwdParams& p, hipStream_t stream) {
+  const int64_t RK = p.Nq * (p.Hq / p.Hkv);
+  const int64_t wgs = (RK + 63) / 64 * p.Hkv * p.B * p.splits;
+  hipLaunchKernelGGL((kv_max_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, 2, CAUSAL, EFQ, true, true>), dim3((unsigned)wgs), dim3(128), 0, stream, p);
+  const int64_t rows = RK * p.Hkv * p.B;
+  hipLaunchKernelGGL((kv_merge_kernel<D, CAUSAL>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -443,6 +606,12 @@ hipError_t launch_d(const FwdParams& p, bool causal, hipStream_t stream) {
   const bool w4 = KV ? p.Nq * (p.Hq / p.Hkv) >= 256 : p.N % 128 == 0;
   if (w4) return causal ? launch<D, 4, true, EFQ, KV>(p, stream) : launch<D, 4, false, EFQ, KV>(p, stream);
   return causal ? launch<D, 2, true, EFQ, KV>(p, stream) : launch<D, 2, false, EFQ, KV>(p, stream);
+}
+
+template <int D>
+hipError_t launch_split_d(const FwdParams& p, bool causal, bool efq, hipStream_t stream) {
+  if (causal) return efq ? launch_split<D, true, true>(p, stream) : launch_split<D, true, false>(p, stream);
+  return efq ? launch_split<D, false, true>(p, stream) : launch_split<D, false, false>(p, stream);
 }
 
 template <bool KV>
@@ -458,7 +627,32 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStrea
 }
 
 hipError_t launch_fwd_kvcache(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream) {
+  if (p.splits > 1) return d == 128 ? launch_split_d<128>(p, causal, efq, stream) : launch_split_d<64>(p, causal, efq, stream);
   return launch_any<true>(p, d, causal, efq, stream);
+}
+
+// Split the key tiles when the one-pass launch would leave the chip mostly idle: fewer than 256
+// workgroups of 64 packed rows (decode, short chunks).  Aim at about 2048 workgroups, at least
+// four tiles per range.
+KvSplit kv_split_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  KvSplit k{1, Nk / 64, 0, 0, 0, 0, 0};
+  const int64_t RK = Nq * (Hq / Hkv);
+  const int64_t base = (RK + 63) / 64 * Hkv * B;
+  const int64_t ntc = Nk / 64;
+  if (base >= 256 || ntc < 8) return k;
+  int64_t s = min((2048 + base - 1) / base, ntc / 4);
+  if (s < 2) return k;
+  k.tps = (ntc + s - 1) / s;
+  k.splits = (ntc + k.tps - 1) / k.tps;
+  if (k.splits < 2) return KvSplit{1, ntc, 0, 0, 0, 0, 0};
+  const int64_t rows = B * Hkv * k.splits * RK;
+  auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+  k.smax = 0;
+  k.m = up(k.smax + rows * 4);
+  k.l = up(k.m + rows * 4);
+  k.o = up(k.l + rows * 4);
+  k.total = up(k.o + rows * d * 4);
+  return k;
 }
 
 }  // namespace attnfp4

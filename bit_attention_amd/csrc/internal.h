@@ -23,7 +23,23 @@ struct FwdParams {
   // head and per-sequence valid lengths (null: every sequence has Nk)
   int64_t Nq, Nk;
   const int32_t* seqlens;
+  // split cache forward (see KvSplit): key tiles split into `splits` ranges of `tps` tiles; the
+  // workspace regions hold, per (b, KV head, split, packed row), the split's largest visible raw
+  // score, its final running max, its row sum and its unnormalised output accumulator
+  int64_t splits, tps;
+  float* ws_smax;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
 };
+
+// How the cache forward splits the key tiles across workgroups (splits == 1: one pass, no
+// workspace) and the byte offsets of its workspace regions (each 256-byte aligned).
+struct KvSplit {
+  int64_t splits, tps;
+  int64_t smax, m, l, o, total;
+};
+KvSplit kv_split_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d);
 
 struct BwdParams {
   const uint8_t* q_codes;

@@ -30,6 +30,7 @@ EXPORTED = (
     "attn_fp4_quantize",
     "attn_fp4_fwd",
     "attn_fp4_fwd_kvcache",
+    "attn_fp4_fwd_kvcache_workspace_bytes",
     "attn_fp4_bwd_workspace_bytes",
     "attn_fp4_bwd_recompute",
 )
@@ -64,6 +65,7 @@ class FwdKvcacheArgs(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("seqlens_k", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
         ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
         ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("d", ctypes.c_int64),
         ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
@@ -106,6 +108,8 @@ def lib():
         L.attn_fp4_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.attn_fp4_fwd_kvcache.restype = ctypes.c_int32
         L.attn_fp4_fwd_kvcache.argtypes = [ctypes.POINTER(FwdKvcacheArgs), ctypes.c_void_p]
+        L.attn_fp4_fwd_kvcache_workspace_bytes.restype = ctypes.c_int64
+        L.attn_fp4_fwd_kvcache_workspace_bytes.argtypes = [ctypes.c_int64] * 6
         L.attn_fp4_bwd_workspace_bytes.restype = ctypes.c_int64
         L.attn_fp4_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 5
         L.attn_fp4_bwd_recompute.restype = ctypes.c_int32
@@ -199,13 +203,20 @@ def attn_fp4_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, causal
     return o, m, l
 
 
+def attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d):
+    return int(lib().attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+
+
 def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k=None,
-                         causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP):
+                         causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP,
+                         workspace="auto"):
     """Forward of Nq new query rows against a pre-quantized key/value cache of capacity Nk.
 
     q_codes [B, Hq, Nq, d/2]; k_codes [B, Hkv, Nk, d/2]; v_codes [B, Hkv, Nk/32, d, 16] (the cache
     quantized as a whole); seqlens_k: int32 device tensor [B] of valid cache lengths, or None for
     Nk.  The new rows are the last Nq positions of each sequence (bottom-right causal alignment).
+    workspace: "auto" allocates the split forward's workspace when the shape uses one; None runs
+    the one-pass kernel; a uint8 CUDA tensor is used as given.
     Returns (o bf16 [B, Hq, Nq, d], m fp32 [B, Hq, Nq], l fp32 [B, Hq, Nq]).
     """
     B, Hq, Nq, dh = q_codes.shape
@@ -230,10 +241,19 @@ def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales
         m = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     if l is None:
         l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
     a = FwdKvcacheArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                        _ptr(v_scales), None if seqlens_k is None else _ptr(seqlens_k),
-                       _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
-                       float(softmax_scale), int(p_rule))
+                       _ptr(o), _ptr(m), _ptr(l),
+                       None if workspace is None else _ptr(workspace),
+                       0 if workspace is None else workspace.numel(),
+                       B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(softmax_scale), int(p_rule))
     _check(lib().attn_fp4_fwd_kvcache(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd_kvcache")
     return o, m, l
 

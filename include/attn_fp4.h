@@ -167,8 +167,18 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
  * per 32-key block exactly as in attn_fp4_fwd, so with Nq = Nk = L_b this is
  * attn_fp4_fwd.  p_rule as for attn_fp4_fwd.
  * Supported: d == 128 or d == 64, Nq >= 1, Nk % 64 == 0, Hq % Hkv == 0.
+ * workspace: optional device memory (256-byte aligned) of at least
+ * attn_fp4_fwd_kvcache_workspace_bytes(...) bytes.  When that size is not 0
+ * (few query rows per KV head: decode, short chunks) and the workspace is
+ * given, the key tiles are split over more workgroups: a first pass finds
+ * each split's largest visible score, each split then starts from the
+ * running max the sequential loop would carry into it (so every P~ code is
+ * the one-pass code), and a last pass merges the splits; only the fp32
+ * summation order of the output differs.  With workspace == NULL the
+ * one-pass kernel runs.  Contents on entry do not matter; clobbered.
  * Errors: ATTN_FP4_E_INVALID_ARG (null/misaligned pointer, bad dims or
- * enum), ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP.
+ * enum), ATTN_FP4_E_WORKSPACE (given but too small or misaligned),
+ * ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP.
  */
 typedef struct {
   const void* q_codes;
@@ -181,11 +191,18 @@ typedef struct {
   void* o;
   float* m;
   float* l;
+  void* workspace;
+  int64_t workspace_bytes;
   int64_t B, Hq, Hkv, Nq, Nk, d;
   int32_t causal;
   float softmax_scale;
   int32_t p_rule;
 } attn_fp4_fwd_kvcache_args;
+
+/* Workspace bytes for the split cache forward of this shape: 0 when the
+ * one-pass kernel is used anyway, -1 for an unsupported shape. */
+int64_t attn_fp4_fwd_kvcache_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                             int64_t d);
 
 int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* args, void* stream);
 

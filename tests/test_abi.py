@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert ops.attn_fp4_abi_version() == 4
+    assert ops.attn_fp4_abi_version() == 5
 
 
 def test_status_strings():
@@ -61,9 +61,18 @@ def test_host_validation_rejects_before_launch():
     for kw in ({"Nk": 96}, {"Nq": 0}, {"Hkv": 3}, {"d": 96}, {"seq": ctypes.c_void_p(258)}, {"p_rule": 2}):
         dims = dict(B=1, Hq=4, Hkv=2, Nq=1, Nk=128, d=128, seq=None, p_rule=0)
         dims.update(kw)
-        a = ops.FwdKvcacheArgs(p, p, p, p, p, p, dims["seq"], p, p, p, dims["B"], dims["Hq"], dims["Hkv"],
-                               dims["Nq"], dims["Nk"], dims["d"], 0, 0.0, dims["p_rule"])
+        a = ops.FwdKvcacheArgs(p, p, p, p, p, p, dims["seq"], p, p, p, None, 0, dims["B"], dims["Hq"],
+                               dims["Hkv"], dims["Nq"], dims["Nk"], dims["d"], 0, 0.0, dims["p_rule"])
         assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 1, kw
+    # split workspace: none needed for many rows; for decode-like shapes a positive size; a given
+    # workspace that is too small is rejected
+    assert L.attn_fp4_fwd_kvcache_workspace_bytes(1, 32, 8, 2048, 32768, 128) == 0
+    need = L.attn_fp4_fwd_kvcache_workspace_bytes(8, 32, 8, 1, 32768, 128)
+    assert need > 0 and need % 256 == 0
+    assert L.attn_fp4_fwd_kvcache_workspace_bytes(1, 4, 3, 1, 128, 128) == -1
+    a = ops.FwdKvcacheArgs(p, p, p, p, p, p, None, p, p, p, ctypes.c_void_p(1 << 20), need - 256,
+                           8, 32, 8, 1, 32768, 128, 0, 0.0, 0)
+    assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 5
     # rows: 3 x [B*Hq*N] fp32; bf16 copies: V^ and K^T per KV head, Q^T and dO^T per query head
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 3 * 1024 + 4 * (2 * 128 * 128 * 2)
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0

@@ -140,3 +140,60 @@ def test_prefill_chunk_full_size_sampled_rows():
         info = check(o[:, h:h + 1, rows], m[:, h:h + 1, rows], l[:, h:h + 1, rows], ro, rm, rl,
                      "prefill chunk head %d" % h)
         print("prefill chunk head %d: rel-L2 %.3e" % (h, info["rel_l2"]))
+
+
+SPLIT_CASES = [
+    # B, Hq, Hkv, Nq, Nk, d, seqlens, causal, p_rule
+    (2, 8, 2, 1, 1024, 128, [1000, 333], True, 0),     # decode, ragged lengths
+    (1, 4, 1, 37, 2048, 64, [1500], True, 0),          # short chunk, d = 64
+    (2, 2, 2, 5, 512, 128, [512, 0], False, 0),        # an empty cache
+    (3, 4, 4, 3, 1024, 128, [2, 700, 1024], True, 0),  # rows with no key next to full ones
+    (2, 8, 2, 2, 1024, 128, [900, 1024], True, 1),     # EFQ
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_Nq%d_Nk%d_d%d_c%d_r%d" % (c[:6] + c[7:]))
+def test_split_small_full(case):
+    import torch
+    from bit_attention_amd import ops
+    B, Hq, Hkv, Nq, Nk, d, seqlens, causal, rule = case
+    assert ops.attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) > 0, "the split path must run"
+    seed = 7300 + sum(case[:6])
+    q = rand_bf16((B, Hq, Nq, d), seed, 1.3)
+    kc = rand_bf16((B, Hkv, Nk, d), seed + 1)
+    vc = rand_bf16((B, Hkv, Nk, d), seed + 2)
+    o, m, l = gpu_kv(q, kc, vc, seqlens, causal, p_rule=rule)
+    ro, rm, rl = oracle.attn_fwd_kvcache(q, kc, vc, seqlens, causal=causal, p_rule="efq" if rule else "exp")
+    info = check(o, m, l, ro, rm, rl, "split " + str(case))
+    print("split %s: rel-L2 %.3e" % (case, info["rel_l2"]))
+    # against the one-pass kernel: the same running maxima (so the same P~ codes), m bit for bit;
+    # O and l differ only by the fp32 summation order
+    args = quantize_cache(q, kc, vc)
+    sl = to_dev(np.asarray(seqlens, dtype=np.int32))
+    o1, m1, l1 = ops.attn_fp4_fwd_kvcache(*args, seqlens_k=sl, causal=causal, p_rule=rule, workspace=None)
+    torch.cuda.synchronize()
+    assert np.array_equal(m1.cpu().numpy(), m)
+    np.testing.assert_allclose(l1.cpu().numpy(), l, rtol=1e-5, atol=0)
+    np.testing.assert_allclose(o1.float().cpu().numpy(), o, rtol=1e-2, atol=1e-3)
+
+
+def test_split_workspace_reuse_and_smaller_call():
+    """The caller's workspace keeps the last call's contents: a second, smaller call must not
+    read stale partial results."""
+    import torch
+    from bit_attention_amd import ops
+    B, Hq, Hkv, Nk, d = 4, 8, 2, 2048, 128
+    need = ops.attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, 2, Nk, d)   # the larger call
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for Nq, seqlens, seed in ((2, [2048, 1900, 1000, 64], 7400), (1, [300, 2048, 7, 1024], 7401)):
+        q = rand_bf16((B, Hq, Nq, d), seed, 1.3)
+        kc = rand_bf16((B, Hkv, Nk, d), seed + 1)
+        vc = rand_bf16((B, Hkv, Nk, d), seed + 2)
+        args = quantize_cache(q, kc, vc)
+        sl = to_dev(np.asarray(seqlens, dtype=np.int32))
+        wsz = ops.attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+        assert 0 < wsz <= need
+        o, m, l = ops.attn_fp4_fwd_kvcache(*args, seqlens_k=sl, causal=True, workspace=ws[:wsz])
+        torch.cuda.synchronize()
+        ro, rm, rl = oracle.attn_fwd_kvcache(q, kc, vc, seqlens, causal=True)
+        check(o.float().cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), ro, rm, rl, "reuse Nq=%d" % Nq)

@@ -67,9 +67,11 @@ __device__ __forceinline__ int slot_key(int s) {
 }
 
 // three waves per SIMD for the 128-row workgroups at d = 128 (<= 168 VGPRs); the 64-row variant
-// keeps more staging registers per thread and runs at two
-template <int D, int W>
-constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
+// keeps more staging registers per thread and runs at two.  The split cache forward (decode:
+// often one wave of a workgroup has rows) runs three stages and three waves per SIMD, so that
+// six workgroups share a CU.
+template <int D, int W, bool SPLIT>
+constexpr int waves_per_simd() { return D == 128 ? (W == 4 || SPLIT ? 3 : 2) : 4; }
 
 // KV selects the cache forward: Nq new query rows per head against a cache of capacity Nk per KV
 // head holding L_b valid keys for sequence b.  New row i sits at position L_b - Nq + i (causal
@@ -85,17 +87,13 @@ constexpr int waves_per_simd() { return D == 128 ? (W == 4 ? 3 : 2) : 4; }
 // kv_merge_kernel.
 template <int D, int W, bool CAUSAL, bool EFQ, bool KV, bool SPLIT>
 __global__ void __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W>(), waves_per_simd<D, W>())))
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D, W, SPLIT>(), waves_per_simd<D, W, SPLIT>())))
 fwd_kernel(FwdParams p) {
   using S = Stage<D>;
   constexpr int NT = 64 * W;                      // threads
   constexpr int KS_STEPS = D / 64;                // MFMA k-steps over the head dim
   constexpr int CT = D / 32;                      // 32-channel output tiles
-#ifndef ATTNFP4_FWD_STAGES
-  constexpr int NSTAGE = 4;                       // LDS stages; tiles are loaded NSTAGE - 1 ahead
-#else
-  constexpr int NSTAGE = ATTNFP4_FWD_STAGES;
-#endif
+  constexpr int NSTAGE = SPLIT ? 3 : 4;            // LDS stages; tiles are loaded NSTAGE - 1 ahead
   constexpr int PD = NSTAGE - 1;
   static_assert(NSTAGE >= 3 && NSTAGE <= 4, "stages");
 
@@ -272,7 +270,7 @@ fwd_kernel(FwdParams p) {
   const int64_t RKs = SPLIT ? p.Nq * G : 0;       // packed rows per KV head (workspace rows)
   if constexpr (SPLIT) {                          // the running max carried into this range
     if (valid)
-      for (int64_t s2 = 0; s2 < sp; ++s2) m_run = fmaxf(m_run, p.ws_smax[(bh * nsp + s2) * RKs + prow]);
+      for (int64_t s2 = 0; s2 < sp; ++s2) m_run = fmaxf(m_run, p.ws_smax[(bh * RKs + prow) * nsp + s2]);
   }
   const float c = p.c;
 
@@ -429,7 +427,7 @@ fwd_kernel(FwdParams p) {
   const float lrow = __uint_as_float(r32[0]);
   if constexpr (SPLIT) {                          // the range's partial results
     if (!valid) return;
-    const int64_t wr = (bh * nsp + sp) * RKs + prow;
+    const int64_t wr = (bh * RKs + prow) * nsp + sp;
     float* orow = p.ws_o + wr * D;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -464,12 +462,14 @@ fwd_kernel(FwdParams p) {
 
 // ---- split cache forward, pass 1: the largest visible raw score per (split, packed row) ----
 // Workgroups of two waves take 64 packed rows and one range of key tiles, as the split forward
-// does; K^ is read straight into the MFMA A operand (no LDS, keys in natural order: the maximum
-// does not depend on where a key sits) and the scores are the forward's, bit for bit (same
-// operands, scales and k-step order).
+// does (when the workgroup has at most 32 rows, both waves take them and alternate tiles).  K^ is
+// read straight into the MFMA A operand, one tile ahead (no LDS; keys in natural order: the
+// maximum does not depend on where a key sits), and the scores are the forward's, bit for bit
+// (same operands, scales and k-step order).
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   constexpr int KS_STEPS = D / 64;
+  __shared__ float xmax[32];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -479,7 +479,9 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   id /= nsp;
   const int64_t bh = id / nqt, qt = id - bh * nqt;
   const int64_t b = bh / p.Hkv, g = bh - b * p.Hkv;
-  const int64_t pr0 = qt * 64, prw = pr0 + 32 * wave, pr = prw + l32;
+  const int64_t pr0 = qt * 64;
+  const bool share = RK - pr0 <= 32;              // one row block, two waves over the tiles
+  const int64_t prw = pr0 + (share ? 0 : 32 * wave), pr = prw + l32;
   const bool valid = pr < RK;
   const int64_t prc = min(pr, RK - 1);
   const int64_t i = prc / G;
@@ -493,8 +495,10 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   const int ntl_all = lim_wg >= 0 ? lim_wg / 64 + 1 : 0;
   const int tb = (int)(sp * p.tps);
   const int te = min(tb + (int)p.tps, min(ntl_all, lim_hi >= 0 ? lim_hi / 64 + 1 : 0));
+  const int tstep = share ? 2 : 1;
   float mx = -__builtin_inff();
-  if (tb < te) {
+  const int t0 = tb + (share ? wave : 0);
+  if (t0 < te) {
     v4i qb[KS_STEPS];
     const uint8_t* qr = p.q_codes + qrow * (D / 2);
 #pragma unroll
@@ -504,23 +508,34 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
     const int64_t kvh = b * p.Hkv + g;
     const auto kc_rs = make_rsrc(p.k_codes + kvh * p.Nk * (D / 2), p.Nk * (D / 2));
     const auto ks_rs = make_rsrc(p.k_scales + kvh * p.Nk * (D / 32), p.Nk * (D / 32));
-    for (int t = tb; t < te; ++t) {
+    // A row l32 of half T is key 64 t + 32 T + l32
+    struct Ops { v4i ka[2][KS_STEPS]; int ksc[2]; };
+    auto load = [&](int t, Ops& o) {
       const int tt = __builtin_amdgcn_readfirstlane(t);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        const int key = 32 * T + l32;             // A row l32 of half T: key 64 t + 32 T + l32
-        v16f acc;
-        int ksc;
+        const int key = 32 * T + l32;
         if constexpr (D == 128)
-          ksc = (int)((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ks_rs, 4 * key, tt * 256, 0) >> (8 * hi));
+          o.ksc[T] = (int)((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ks_rs, 4 * key, tt * 256, 0) >> (8 * hi));
         else
-          ksc = (int)__builtin_amdgcn_raw_buffer_load_b8(ks_rs, 2 * key + hi, tt * 128, 0);
-        const v4i ka0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kc_rs, key * (D / 2) + 16 * hi, tt * (64 * D / 2), 0));
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
-        if constexpr (KS_STEPS == 2) {
-          const v4i ka1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kc_rs, key * (D / 2) + 32 + 16 * hi, tt * (64 * D / 2), 0));
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka1), widen(qb[1]), acc, 4, 4, 2, ksc, 2, qsc);
-        }
+          o.ksc[T] = (int)__builtin_amdgcn_raw_buffer_load_b8(ks_rs, 2 * key + hi, tt * 128, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS_STEPS; ++ks)
+          o.ka[T][ks] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    kc_rs, key * (D / 2) + 32 * ks + 16 * hi, tt * (64 * D / 2), 0));
+      }
+    };
+    Ops cur, nxt;
+    load(t0, cur);
+    for (int t = t0; t < te; t += tstep) {
+      if (t + tstep < te) load(t + tstep, nxt);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        v16f acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(cur.ka[T][0]), widen(qb[0]), v16f{}, 4, 4, 0,
+                                                                   cur.ksc[T], 0, qsc);
+        if constexpr (KS_STEPS == 2)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(cur.ka[T][1]), widen(qb[1]), acc, 4, 4, 2,
+                                                                cur.ksc[T], 2, qsc);
         // register r holds key 64 t + 32 T + 8 (r / 4) + 4 hi + r % 4 of query l32
         if (t * 64 + 63 > lim_lo) {
 #pragma unroll
@@ -530,23 +545,34 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
       }
+      cur = nxt;
     }
   }
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
   mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  if (valid && hi == 0) p.ws_smax[(bh * nsp + sp) * RK + pr] = mx;
+  if (share) {                                    // combine the two waves' tiles
+    if (wave == 1 && hi == 0) xmax[l32] = mx;
+    __syncthreads();
+    if (wave == 1) return;
+    mx = fmaxf(mx, xmax[l32]);
+  }
+  if (valid && hi == 0) p.ws_smax[(bh * RK + pr) * nsp + sp] = mx;
 }
 
 // ---- split cache forward, pass 3: merge the ranges' partial results into O, m, l ----
-// One wave per packed row.  With M the largest running max over the ranges, range s contributes
+// One workgroup per packed row; the partial results of a row are contiguous ([row][range] and
+// [row][range][d]).  With M the largest running max over the ranges, range s contributes
 // exp2((m_s - M) c) times its accumulator and row sum: the sequential loop's history rescaling
-// written as one factor per range.
+// written as one factor per range.  Each wave takes every fourth range.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) kv_merge_kernel(FwdParams p) {
+  constexpr int CPL = D / 64;                     // channels per lane
+  __shared__ float red_o[4][D];
+  __shared__ float red_l[4];
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t G = p.Hq / p.Hkv, RK = p.Nq * G, nsp = p.splits;
-  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (rid >= p.B * p.Hkv * RK) return;
+  const int64_t rid = blockIdx.x;
   const int64_t bh = rid / RK, pr = rid - bh * RK;
   const int64_t b = bh / p.Hkv, g = bh - b * p.Hkv;
   const int64_t i = pr / G;
@@ -555,20 +581,33 @@ __global__ void __launch_bounds__(256) kv_merge_kernel(FwdParams p) {
   const int64_t len = p.seqlens != nullptr ? min(max((int64_t)p.seqlens[b], (int64_t)0), p.Nk) : p.Nk;
   const int64_t last = min((pr / 64) * 64 + 63, RK - 1);
   const int64_t lim_wg = CAUSAL ? min(len - p.Nq + last / G, len - 1) : len - 1;
-  const int64_t nr = lim_wg >= 0 ? (lim_wg / 64) / p.tps + 1 : 0;
+  const int nr = lim_wg >= 0 ? (int)((lim_wg / 64) / p.tps + 1) : 0;
+  const float* wm = p.ws_m + rid * nsp;
+  const float* wl = p.ws_l + rid * nsp;
+  const float* wo = p.ws_o + rid * nsp * D + CPL * lane;
   float M = -__builtin_inff();
-  for (int64_t s = 0; s < nr; ++s) M = fmaxf(M, p.ws_m[(bh * nsp + s) * RK + pr]);
-  constexpr int CPL = D / 64;                       // channels per lane
+  for (int s = 0; s < nr; ++s) M = fmaxf(M, wm[s]);
   float acc[CPL] = {};
   float lt = 0.0f;
   if (M != -__builtin_inff()) {
-    for (int64_t s = 0; s < nr; ++s) {
-      const int64_t wr = (bh * nsp + s) * RK + pr;
-      const float w = __builtin_amdgcn_exp2f((p.ws_m[wr] - M) * p.c);
-      lt += w * p.ws_l[wr];
+#pragma unroll 4
+    for (int s = wave; s < nr; s += 4) {
+      const float w = __builtin_amdgcn_exp2f((wm[s] - M) * p.c);
+      lt += w * wl[s];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] += w * p.ws_o[wr * D + CPL * lane + k];
+      for (int k = 0; k < CPL; ++k) acc[k] += w * wo[(int64_t)s * D + k];
     }
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) red_o[wave][CPL * lane + k] = acc[k];
+  if (lane == 0) red_l[wave] = lt;
+  __syncthreads();
+  if (wave != 0) return;
+  lt = red_l[0] + red_l[1] + red_l[2] + red_l[3];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int ch = CPL * lane + k;
+    acc[k] = red_o[0][ch] + red_o[1][ch] + red_o[2][ch] + red_o[3][ch];
   }
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   uint16_t* orow = p.o + qrow * D + CPL * lane;
@@ -595,7 +634,7 @@ hipError_t launch_split(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((kv_max_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(128), 0, stream, p);
   hipLaunchKernelGGL((fwd_kernel<D, 2, CAUSAL, EFQ, true, true>), dim3((unsigned)wgs), dim3(128), 0, stream, p);
   const int64_t rows = RK * p.Hkv * p.B;
-  hipLaunchKernelGGL((kv_merge_kernel<D, CAUSAL>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((kv_merge_kernel<D, CAUSAL>), dim3((unsigned)rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

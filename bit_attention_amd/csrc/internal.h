@@ -24,7 +24,7 @@ struct FwdParams {
   int64_t Nq, Nk;
   const int32_t* seqlens;
   // split cache forward (see KvSplit): key tiles split into `splits` ranges of `tps` tiles; the
-  // workspace regions hold, per (b, KV head, split, packed row), the split's largest visible raw
+  // workspace regions hold, per (b, KV head, packed row, split), the split's largest visible raw
   // score, its final running max, its row sum and its unnormalised output accumulator
   int64_t splits, tps;
   float* ws_smax;

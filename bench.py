@@ -7,8 +7,9 @@ HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
 
 Printed: one JSON line with the step throughput, a roofline object for the dominant kernel (the
 fused forward, timed alone with HIP events on the stream it runs on), the backward of the QAT
-workload (B=1, H=16, N=8192, d=128) measured the same way, and the CPU oracle timed on a bounded
-sample of the same workload.
+workload (B=1, H=16, N=8192, d=128) measured the same way, the forward with the exp-free EFQ
+probability codes, the cache forward on a decode batch and a chunked-prefill step, and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
@@ -30,7 +31,7 @@ QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 # Measured HBM traffic of one forward launch at the bench shape: rocprofv3 --pmc FETCH_SIZE and
 # --pmc WRITE_SIZE, each scaled by the factor the same counter shows on a plain 1 GiB device copy
 # (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source it was measured on.
-FWD_TRAFFIC = {"source_sha1": "09ad48f5849896b1a3bebc8424b42ac5cc5c026e", "bytes": 1.057e9}
+FWD_TRAFFIC = {"source_sha1": "cf6fb7eee089d4b68f586e8c748067e09ad61483", "bytes": 1.04e9}
 
 
 def fwd_source_sha1():
@@ -68,6 +69,28 @@ def _gen_one(a):
     from bit_attention_amd import workloads as W
     name, t, b, h = a
     return W.gen_head(W.WORKLOADS[name], t, b, h)
+
+
+def _gen_cache_one(a):
+    from bit_attention_amd import workloads as W
+    name, t, b, h = a
+    return W.gen_cache_head(W.CACHE_WORKLOADS[name], t, b, h)
+
+
+def gen_cache_inputs(w, torch):
+    """Seeded inputs of a cache workload as bf16 device tensors: q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d]."""
+    import numpy as np
+    from concurrent.futures import ProcessPoolExecutor
+    out = {}
+    with ProcessPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        for t in ("q", "k", "v"):
+            H, n = (w.Hq, w.Nq) if t == "q" else (w.Hkv, w.Nk)
+            jobs = [(b, h) for b in range(w.B) for h in range(H)]
+            dev = torch.empty((w.B, H, n, w.d), dtype=torch.bfloat16, device="cuda")
+            for (b, h), x in zip(jobs, ex.map(_gen_cache_one, [(w.name, t, b, h) for b, h in jobs])):
+                dev[b, h] = torch.from_numpy(x).to(torch.bfloat16)
+            out[t] = dev
+    return out
 
 
 def time_region(fn, reps, stream):
@@ -144,6 +167,51 @@ def bench_backward(args, torch, ops, W):
             "tflops_total": (fp4 + bf16) / ms / 1e9, "roofline_ms": t_roof, "frac": t_roof / ms}
 
 
+def bench_kvcache(args, torch, ops, W, only=None):
+    """The cache forward (attn_fp4_fwd_kvcache) on the decode and chunked-prefill workloads: the
+    forward alone (K^/V^ already quantized in the cache), HIP events on its stream."""
+    import numpy as np
+    out = {}
+    for name, w in W.CACHE_WORKLOADS.items():
+        if only is not None and name not in only:
+            continue
+        x = gen_cache_inputs(w, torch)
+        qq = ops.attn_fp4_quantize(x["q"], 0)
+        kq = ops.attn_fp4_quantize(x["k"], 0)
+        vq = ops.attn_fp4_quantize(x["v"], 1)
+        del x
+        lens = W.cache_lengths(w)
+        sl = torch.from_numpy(lens).cuda()
+        o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+        m = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        need = ops.attn_fp4_fwd_kvcache_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need > 0 else None
+        fn = lambda: ops.attn_fp4_fwd_kvcache(*qq, *kq, *vq, seqlens_k=sl, causal=w.causal, o=o, m=m, l=l,
+                                              workspace=ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = time_region(fn, max(10, args.steps), torch.cuda.current_stream())
+        lens64 = lens.astype(np.int64)
+        pairs = 0
+        for L in lens64:
+            pos = L - w.Nq + np.arange(w.Nq)
+            vis = np.minimum(pos + 1, L) if w.causal else np.full(w.Nq, L)
+            pairs += int(np.maximum(vis, 0).sum()) * w.Hq
+        # algorithmic bytes: the valid part of the cache (K^ and V^ codes and scales) once, Q^ once,
+        # O (bf16) and m, l written once
+        cache_b = int(lens64.sum()) * w.Hkv * 2 * (w.d // 2 + w.d // 32)
+        io_b = w.B * w.Hq * w.Nq * (w.d // 2 + w.d // 32 + 2 * w.d + 8)
+        out[name] = {"ms": ms, "split": need > 0, "visible_pairs": pairs,
+                     "tflops": 4.0 * w.d * pairs / ms / 1e9,
+                     "frac_mfma": 4.0 * w.d * pairs / ms / 1e9 / PEAK_FP4_TFLOPS,
+                     "bytes": cache_b + io_b, "gbps": (cache_b + io_b) / ms / 1e6,
+                     "frac_hbm": (cache_b + io_b) / ms / 1e6 / PEAK_HBM_GBS,
+                     "cache_lengths": "seeded U[%d, %d]" % (w.len_lo, w.Nk)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +223,8 @@ def main():
                     help="if > 0: only run the forward kernel this many times (for profilers)")
     ap.add_argument("--bwd-only-reps", type=int, default=0,
                     help="if > 0: only run the QAT-workload backward this many times (for profilers)")
+    ap.add_argument("--kv-only-reps", type=int, default=0,
+                    help="if > 0: only run the decode cache forward this many times (for profilers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="if > 0: only run a plain device copy of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiler)")
@@ -182,6 +252,11 @@ def main():
     if args.bwd_only_reps > 0:
         args.steps = args.bwd_only_reps
         log("backward", bench_backward(args, torch, ops, W))
+        return
+
+    if args.kv_only_reps > 0:
+        args.steps = args.kv_only_reps
+        log("kvcache", bench_kvcache(args, torch, ops, W, only=["decode_b8hq32hkv8nk32768d128"]))
         return
 
     w = W.WORKLOADS["dit_b1h24n32768d128"]
@@ -236,6 +311,8 @@ def main():
     # dominant kernel alone (same launch configuration), HIP events on its stream
     fwd_ms = time_region(fwd, args.steps, stream)
     quant_ms = time_region(quantize, args.steps, stream)
+    efq_ms = time_region(lambda: ops.attn_fp4_fwd(qc, qs, kc, ks, vc, vs, causal=w.causal, o=o, m=m, l=l,
+                                                  p_rule=ops.P_EFQ), args.steps, stream)
     flops = 4.0 * B * H * N * N * d
     fwd_tflops = flops / fwd_ms / 1e9
     log("fwd kernel %.3f ms = %.1f TFLOPS; quantize q,k,v %.3f ms" % (fwd_ms, fwd_tflops, quant_ms))
@@ -265,9 +342,14 @@ def main():
                      "gbps": QUANT_BYTES_PER_ELEM * 3 * B * H * N * d / quant_ms / 1e6,
                      "frac_hbm": QUANT_BYTES_PER_ELEM * 3 * B * H * N * d / quant_ms / 1e6 / PEAK_HBM_GBS},
     }
+    result["efq"] = {"ms": efq_ms, "tflops": flops / efq_ms / 1e9, "frac": flops / efq_ms / 1e9 / PEAK_FP4_TFLOPS,
+                     "p_rule": "exp-free EFQ codes (a reading of the pages; not the headline definition)"}
+    del dev
     if not args.no_backward:
         result["backward"] = bench_backward(args, torch, ops, W)
         log("backward", result["backward"])
+    result["kvcache"] = bench_kvcache(args, torch, ops, W)
+    log("kvcache", result["kvcache"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w)

@@ -141,13 +141,32 @@ __device__ __forceinline__ int p_scale_byte(float tb, float mq) {
   return max((int)(__float_as_uint(pm) >> 23) - 2, 1);
 }
 
+// Four transposing LDS loads (ds_read_b64_tr_b16) and the wait for them, in one statement: the
+// results are complete when it ends.  (The builtin form makes the compiler wait for every direct
+// global-to-LDS load in flight first, which would serialise the staging of the next tiles.)
+__device__ __forceinline__ void lds_read_tr4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, v2i& r0, v2i& r1,
+                                             v2i& r2, v2i& r3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+}
+
 // ---------------------------------------------------------------------------------------------
 // 3. dK / dV.  Workgroup = W waves; wave w: pair p = w/2 owns keys k0 + 32p + [0, 32), half = w%2
 // takes query sub-tile `half` in the elementwise phase and channel half `half` in the products.
-// The query tile's operands are staged by direct global -> LDS loads in two groups that alternate
-// with the two phases of a tile: group A (Q^ codes and scales, the row constants, dO) is read by
-// the elementwise phase and refilled for the next tile during the products; group B (dO^T, Q^T)
-// is read by the products and refilled during the next elementwise phase.
+// The query tile's operands are staged by direct global -> LDS loads in two groups, each double
+// buffered: group A (Q^ codes and scales, the row constants, dO) is read by the elementwise phase,
+// group B (dO^T, Q^T) by the products.  The products phase of tile n issues group A of tile n + 2
+// and group B of tile n + 1, so that every load has about a whole tile to land before the one
+// wait per tile (ahead of the products).  A = P~/l and dS pass from the elementwise phase to the
+// products query-major ([64 q][KEYS], 16-byte chunks swizzled by the row): a lane writes its 16
+// keys of one query as two 16-byte stores, and the products read them back as [key][query]
+// operands with the transposing LDS load.
 template <int D, int W>
 struct DkdvLds {
   static constexpr int KEYS = 16 * W;                 // 32 keys per pair of waves
@@ -155,11 +174,25 @@ struct DkdvLds {
   static constexpr int QS = QC + 64 * D / 2;          // A: Q^ scales [64 q] dwords
   static constexpr int ROWS = QS + 64 * 4;            // A: mq, il, D: 3 x [64] floats
   static constexpr int DO = ROWS + 3 * 64 * 4;        // A: dO bf16 [64 q][D], swizzled chunks
-  static constexpr int DOT = DO + 64 * D * 2;         // B: dO^T bf16 [D][64 q], swizzled chunks
+  static constexpr int A_BYTES = DO + 64 * D * 2;
+  static constexpr int DOT = 0;                       // B: dO^T bf16 [D][64 q], swizzled chunks
   static constexpr int QT = DOT + D * 64 * 2;         // B: Q^T bf16 [D][64 q], swizzled chunks
-  static constexpr int PS = QT + D * 64 * 2;          // A = P~/l bf16 [KEYS][64 q], swizzled chunks
-  static constexpr int DS = PS + KEYS * 64 * 2;       // dS bf16 [KEYS][64 q]
-  static constexpr int BYTES = DS + KEYS * 64 * 2;
+  static constexpr int B_BYTES = QT + D * 64 * 2;
+  static constexpr int A0 = 0;                        // two group-A buffers, then two group-B
+  static constexpr int B0 = 2 * A_BYTES;
+  static constexpr int PS = B0 + 2 * B_BYTES;         // A = P~/l bf16 [64 q][KEYS], swizzled chunks
+  static constexpr int DS = PS + 64 * KEYS * 2;       // dS bf16 [64 q][KEYS]
+  static constexpr int BYTES = DS + 64 * KEYS * 2;
+  static constexpr int NCH = KEYS / 8;                // 16-byte chunks per scratch row
+  static_assert(NCH == 8 || NCH == 16, "scratch swizzle");
+  // byte offset of (query row q, key chunk c) in the scratch.  The chunk is XORed with bits of the
+  // row so that both access patterns spread over all banks: a lane's two 16-byte stores (32 rows
+  // of one chunk per instruction) and the transposing loads (4 consecutive rows x 4 chunks per
+  // 16 lanes, two such row groups 8 apart per instruction).
+  static __device__ __forceinline__ int chunk(int q, int c) {
+    const int x = NCH == 16 ? (((q & 3) << 2) | ((q >> 2) & 3)) : (((q & 3) << 1) | ((q >> 2) & 1));
+    return q * (KEYS * 2) + 16 * (c ^ x);
+  }
 };
 
 template <int D, int W, bool CAUSAL>
@@ -240,7 +273,7 @@ bwd_dkdv_kernel(BwdParams p) {
     const int cidx = 64 * (kind == 6 ? j : j - NB / 2) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
     return (uint32_t)ch * (uint32_t)(N * 2) + 16 * cc;
   };
-  auto dst_of = [](int kind, int j) -> int {
+  auto dst_of = [](int kind, int j) -> int {   // within the group's buffer
     return kind == 0 ? L::QC + 1024 * j : kind == 1 ? L::DO + 1024 * (j - NQC) : kind == 2 ? L::QS
          : kind <= 5 ? L::ROWS + 256 * (kind - 3) : kind == 6 ? L::DOT + 1024 * j : L::QT + 1024 * (j - NB / 2);
   };
@@ -255,8 +288,9 @@ bwd_dkdv_kernel(BwdParams p) {
     for (int i = 0; i < JB; ++i) { const int j = min(wave + W * i, NB - 1); goff_b[i] = goff_of(kind_b(j), j); }
   }
   // row offsets of query tile (hh, q0) in elements: along the rows of [head][N] and of [head][D][N]
-  auto issue = [&](int kind, int j, uint32_t goff, int64_t hh, int64_t q0) __attribute__((always_inline)) {
-    auto* dst = (__attribute__((address_space(3))) void*)(smem + dst_of(kind, j));   // LDS-DMA target
+  auto issue = [&](int kind, int j, uint32_t goff, int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
+    const int base = kind <= 5 ? L::A0 + buf * L::A_BYTES : L::B0 + buf * L::B_BYTES;
+    auto* dst = (__attribute__((address_space(3))) void*)(smem + base + dst_of(kind, j));   // LDS-DMA target
     const int r = __builtin_amdgcn_readfirstlane((int)(hh * N + q0));                  // row of [head][N]
     const int tcol = __builtin_amdgcn_readfirstlane((int)(hh * D * N + q0));          // element of [head][D][N]
     switch (kind) {
@@ -273,24 +307,24 @@ bwd_dkdv_kernel(BwdParams p) {
       default: __builtin_amdgcn_raw_ptr_buffer_load_lds(qt_rs, dst, 16, (int)goff, tcol * 2, 0, 0); break;
     }
   };
-  auto issue_a = [&](int64_t hh, int64_t q0) __attribute__((always_inline)) {
+  auto issue_a = [&](int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < JA; ++i) {
       const int j = min(wave + W * i, NA - 1);
       uint32_t goff;
       if constexpr (PRE_A) goff = goff_a[PRE_A ? i : 0];
       else goff = goff_of(kind_a(j), j);
-      issue(kind_a(j), j, goff, hh, q0);
+      issue(kind_a(j), j, goff, hh, q0, buf);
     }
   };
-  auto issue_b = [&](int64_t hh, int64_t q0) __attribute__((always_inline)) {
+  auto issue_b = [&](int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < JB; ++i) {
       const int j = min(wave + W * i, NB - 1);
       uint32_t goff;
       if constexpr (PRE_B) goff = goff_b[PRE_B ? i : 0];
       else goff = goff_of(kind_b(j), j);
-      issue(kind_b(j), j, goff, hh, q0);
+      issue(kind_b(j), j, goff, hh, q0, buf);
     }
   };
 
@@ -298,23 +332,34 @@ bwd_dkdv_kernel(BwdParams p) {
   const int64_t j_first = CAUSAL ? k0 / 64 : 0;   // query tiles below the keys see none of them
   const int64_t nj = N / 64 - j_first;
   const int64_t ntile = group * nj;
-  issue_a(0, j_first * 64);
+  // query tile n as (head of the group hh, tile jj): the tiles of a head are consecutive
+  auto next = [&](int64_t& h_, int64_t& j_) __attribute__((always_inline)) {
+    if (++j_ == nj) { j_ = 0; ++h_; }
+  };
+  int64_t hh = 0, jj = 0;                          // tile n
+  int64_t hn = 0, jn = 0;                          // tile n + 1
+  next(hn, jn);
+  issue_a(0, j_first * 64, 0);
+  issue_b(0, j_first * 64, 0);
+  if (ntile > 1) issue_a(hn, (j_first + jn) * 64, 1);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int64_t n = 0; n < ntile; ++n) {
-    const int64_t hh = n / nj;
-    const int64_t q0 = (j_first + (n - hh * nj)) * 64;
-    const int64_t h = g * group + hh;
-    const int64_t bh = b * p.Hq + h;
-    (void)bh;
-    issue_b(hh, q0);
+  // one tile; the buffer index is a compile-time constant (the loop below is unrolled by two) so
+  // that the compiler sees which LDS bytes the direct loads write and adds no waits of its own
+  auto tile = [&](auto bufc, int64_t n) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    const int64_t q0 = (j_first + jj) * 64;
+    int64_t h2 = hn, j2 = jn;                       // tile n + 2
+    next(h2, j2);
+    const uint8_t* sa = smem + L::A0 + buf * L::A_BYTES;
+    const uint8_t* sb = smem + L::B0 + buf * L::B_BYTES;
 
     // ---- elementwise phase: keys kp + [0,32) x queries q0 + 32 half + [0,32) ----
     {
       const int ql = 32 * half + l32;                  // this lane's query within the tile
       const int64_t qrow = q0 + ql;
       // S^T = K^ Q^T (FP4)
-      const uint8_t* qcl = smem + L::QC + ql * (D / 2);
-      const uint32_t qsw = *reinterpret_cast<const uint32_t*>(smem + L::QS + 4 * ql);
+      const uint8_t* qcl = sa + L::QC + ql * (D / 2);
+      const uint32_t qsw = *reinterpret_cast<const uint32_t*>(sa + L::QS + 4 * ql);
       const int qsc = (int)(qsw >> (8 * hi));
       v16f st = v16f{};
       st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi)),
@@ -327,12 +372,12 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int s = 0; s < DS_STEPS; ++s) {
         const int cc = 2 * s + hi;
-        const v4i bo = *reinterpret_cast<const v4i*>(smem + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, RC)));
+        const v4i bo = *reinterpret_cast<const v4i*>(sa + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, RC)));
         dp = mfma_bf16(va[s], bo, dp);
       }
-      const float mq = reinterpret_cast<const float*>(smem + L::ROWS)[ql];
-      const float il = reinterpret_cast<const float*>(smem + L::ROWS)[64 + ql];
-      const float dd = reinterpret_cast<const float*>(smem + L::ROWS)[128 + ql];
+      const float mq = reinterpret_cast<const float*>(sa + L::ROWS)[ql];
+      const float il = reinterpret_cast<const float*>(sa + L::ROWS)[64 + ql];
+      const float dd = reinterpret_cast<const float*>(sa + L::ROWS)[128 + ql];
       // register r holds key kp + 16 hi + r
       if (CAUSAL) {
         const int jrel = (int)(qrow - kp) - 16 * hi;
@@ -345,8 +390,8 @@ bwd_dkdv_kernel(BwdParams p) {
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const int sb = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
-      const float sc = __uint_as_float((uint32_t)sb << 23);
+      const int sbyte = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
+      const float sc = __uint_as_float((uint32_t)sbyte << 23);
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -mq));
@@ -366,45 +411,63 @@ bwd_dkdv_kernel(BwdParams p) {
         sw8[2 * q] = pk_bf16(ds[0], ds[1]);
         sw8[2 * q + 1] = pk_bf16(ds[2], ds[3]);
       }
-      // [key][query] scratch: key row 32 pair + 16 hi + r, query column ql
-      uint16_t* ps = reinterpret_cast<uint16_t*>(smem + L::PS);
-      uint16_t* dsp = reinterpret_cast<uint16_t*>(smem + L::DS);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * pair + 16 * hi + r;
-        const int col = 8 * ((ql >> 3) ^ swz_big(key, 8)) + (ql & 7);
-        const uint32_t a = aw[r >> 1], s2 = sw8[r >> 1];
-        ps[key * 64 + col] = (uint16_t)((r & 1) ? (a >> 16) : (a & 0xFFFF));
-        dsp[key * 64 + col] = (uint16_t)((r & 1) ? (s2 >> 16) : (s2 & 0xFFFF));
-      }
+      // query-major scratch: row ql, keys 32 pair + 16 hi + [0, 16) = chunks 4 pair + 2 hi + {0, 1}
+      const int c0 = 4 * pair + 2 * hi;
+      *reinterpret_cast<v4i*>(smem + L::PS + L::chunk(ql, c0)) = v4i{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3]};
+      *reinterpret_cast<v4i*>(smem + L::PS + L::chunk(ql, c0 + 1)) = v4i{(int)aw[4], (int)aw[5], (int)aw[6], (int)aw[7]};
+      *reinterpret_cast<v4i*>(smem + L::DS + L::chunk(ql, c0)) = v4i{(int)sw8[0], (int)sw8[1], (int)sw8[2], (int)sw8[3]};
+      *reinterpret_cast<v4i*>(smem + L::DS + L::chunk(ql, c0 + 1)) = v4i{(int)sw8[4], (int)sw8[5], (int)sw8[6], (int)sw8[7]};
     }
-    // group B of this tile has landed (each wave waits for its own loads); group A is free
+    // group B of this tile (and group A of the next) has landed; the scratch is written
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (n + 1 < ntile) {
-      const int64_t hn = (n + 1) / nj;
-      issue_a(hn, (j_first + (n + 1 - hn * nj)) * 64);
-    }
 
     // ---- products: dV^T += dO^T A, dK^T += Q^T dS over the tile's 64 queries ----
     {
-      const int key = 32 * pair + l32;
+      // transposing reads of the query-major scratch: in each 16-lane group, lane i supplies
+      // keys kb + 4 (i % 4) + [0, 4) of query row qb + i / 4, and lane j receives key kb + j of
+      // rows qb .. qb + 3; the group's keys kb = 32 pair + 16 (lane / 16 % 2), its rows start at
+      // 16 s + 8 hi + 4 t
+      const int gi = lane & 15;
+      const int kst = 32 * pair + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+      auto tr_addr = [&](int region, int qrw) -> uint32_t {
+        return lds0 + (uint32_t)(region + L::chunk(qrw, kst >> 3) + 2 * (kst & 7));
+      };
+      // group A of tile n + 2 (into this tile's A buffer, read by the elementwise phase that has
+      // ended) and group B of tile n + 1 (into the other B buffer, free since tile n - 1)
+      if (n + 2 < ntile) issue_a(h2, (j_first + j2) * 64, buf);
+      if (n + 1 < ntile) issue_b(hn, (j_first + jn) * 64, 1 - buf);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const int qa = 16 * s + 8 * hi + (gi >> 2);   // rows of the two transposing loads: qa, qa + 4
+        v2i p0, p1, s0, s1;
+        lds_read_tr4(tr_addr(L::PS, qa), tr_addr(L::PS, qa + 4), tr_addr(L::DS, qa), tr_addr(L::DS, qa + 4), p0, p1,
+                     s0, s1);
+        const v4i bp = v4i{p0[0], p0[1], p1[0], p1[1]};
+        const v4i bs = v4i{s0[0], s0[1], s1[0], s1[1]};
         const int cc = 2 * s + hi;                    // queries 16 s + 8 hi + [0, 8)
-        const v4i bp = *reinterpret_cast<const v4i*>(smem + L::PS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
-        const v4i bs = *reinterpret_cast<const v4i*>(smem + L::DS + key * 128 + 16 * (cc ^ swz_big(key, 8)));
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int ch = CH * half + 32 * ct + l32;
-          const v4i ao = *reinterpret_cast<const v4i*>(smem + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
-          const v4i aq = *reinterpret_cast<const v4i*>(smem + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+          const v4i ao = *reinterpret_cast<const v4i*>(sb + L::DOT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
+          const v4i aq = *reinterpret_cast<const v4i*>(sb + L::QT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
           dv[ct] = mfma_bf16(ao, bp, dv[ct]);
           dk[ct] = mfma_bf16(aq, bs, dk[ct]);
         }
       }
     }
-    // group A of the next tile has landed; group B and the scratch are free
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the scratch and this tile's B buffer are free (group A of tile n + 1 landed before the
+    // products); the loads issued above stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    hh = hn;
+    jj = jn;
+    hn = h2;
+    jn = j2;
+  };
+  for (int64_t n = 0; n < ntile; n += 2) {
+    tile(std::integral_constant<int, 0>{}, n);
+    if (n + 1 >= ntile) break;
+    tile(std::integral_constant<int, 1>{}, n + 1);
   }
 
   // ---- store: lane holds key kp + l32, channels CH half + 32 ct + 8 a + 4 hi + [0,4) ----

@@ -671,15 +671,17 @@ hipError_t launch_fwd_kvcache(const FwdParams& p, int d, bool causal, bool efq, 
 }
 
 // Split the key tiles when the one-pass launch would leave the chip mostly idle: fewer than 256
-// workgroups of 64 packed rows (decode, short chunks).  Aim at about 2048 workgroups, at least
-// four tiles per range.
+// workgroups of 64 packed rows (decode, short chunks).  Aim at about 1024 workgroups per pass (four
+// per CU; measured best for decode against 512, 768, 1280, 1536, 2048 and 4096: fewer, longer
+// ranges keep each workgroup's loads streaming, more ranges add fixed costs), at least four tiles
+// per range.
 KvSplit kv_split_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
   KvSplit k{1, Nk / 64, 0, 0, 0, 0, 0};
   const int64_t RK = Nq * (Hq / Hkv);
   const int64_t base = (RK + 63) / 64 * Hkv * B;
   const int64_t ntc = Nk / 64;
   if (base >= 256 || ntc < 8) return k;
-  int64_t s = min((2048 + base - 1) / base, ntc / 4);
+  int64_t s = min((1024 + base - 1) / base, ntc / 4);
   if (s < 2) return k;
   k.tps = (ntc + s - 1) / s;
   k.splits = (ntc + k.tps - 1) / k.tps;

@@ -81,6 +81,8 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* a, void* stream) {
     if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
   if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
   if (a->p_rule != ATTN_FP4_P_EXP && a->p_rule != ATTN_FP4_P_EFQ) return ATTN_FP4_E_INVALID_ARG;
+  // the kernels address one KV head's K^ / V^ codes with 32-bit buffer offsets
+  if (a->N * a->d / 2 > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_UNSUPPORTED;
   st = check_device();
   if (st != ATTN_FP4_OK) return st;
   attnfp4::FwdParams p;
@@ -114,10 +116,10 @@ static int32_t check_kvcache_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0) return ATTN_FP4_E_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_FP4_E_INVALID_ARG;
   if (Nk % 64 != 0 || Hq % Hkv != 0) return ATTN_FP4_E_INVALID_ARG;
-  // 32-bit buffer offsets within one KV head's cache, and the grid: at most one workgroup per
-  // 64 packed query rows (times the splits)
-  if (Nk * d > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  // the grid: at most one workgroup per 64 packed query rows (times the splits)
   if ((Nq * (Hq / Hkv) + 63) / 64 * Hkv * B * (Nk / 64) > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  // the kernels address one KV head's cache codes with 32-bit buffer offsets
+  if (Nk * d / 2 > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_UNSUPPORTED;
   return ATTN_FP4_OK;
 }
 

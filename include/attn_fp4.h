@@ -140,7 +140,9 @@ enum { ATTN_FP4_P_EXP = 0, ATTN_FP4_P_EFQ = 1 };
  * on the scaled FP4 matrix cores; the running max, running sum and the
  * output accumulator are fp32.  Bitwise deterministic.
  * Errors: ATTN_FP4_E_INVALID_ARG (null/misaligned pointer, bad dims),
- * ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP (launch failure).
+ * ATTN_FP4_E_UNSUPPORTED (N * d / 2 above 2^31 - 1: one head's codes exceed the
+ * kernels' 32-bit buffer offsets), ATTN_FP4_E_UNSUPPORTED_DEVICE,
+ * ATTN_FP4_E_HIP (launch failure).
  */
 int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
 
@@ -177,7 +179,8 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
  * summation order of the output differs.  With workspace == NULL the
  * one-pass kernel runs.  Contents on entry do not matter; clobbered.
  * Errors: ATTN_FP4_E_INVALID_ARG (null/misaligned pointer, bad dims or
- * enum), ATTN_FP4_E_WORKSPACE (given but too small or misaligned),
+ * enum), ATTN_FP4_E_UNSUPPORTED (Nk * d / 2 above 2^31 - 1),
+ * ATTN_FP4_E_WORKSPACE (given but too small or misaligned),
  * ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP.
  */
 typedef struct {

@@ -73,6 +73,12 @@ def test_host_validation_rejects_before_launch():
     a = ops.FwdKvcacheArgs(p, p, p, p, p, p, None, p, p, p, ctypes.c_void_p(1 << 20), need - 256,
                            8, 32, 8, 1, 32768, 128, 0, 0.0, 0)
     assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 5
+    # one head's codes beyond the kernels' 32-bit buffer offsets: unsupported, before any launch
+    big = 1 << 26
+    a = ops.FwdArgs(p, p, p, p, p, p, p, p, p, 1, 1, 1, big, 128, 0, 0.0, 0)
+    assert L.attn_fp4_fwd(ctypes.byref(a), None) == 3
+    a = ops.FwdKvcacheArgs(p, p, p, p, p, p, None, p, p, p, None, 0, 1, 1, 1, 1, big, 128, 0, 0.0, 0)
+    assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 3
     # rows: 3 x [B*Hq*N] fp32; bf16 copies: V^ and K^T per KV head, Q^T and dO^T per query head
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 3 * 1024 + 4 * (2 * 128 * 128 * 2)
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0

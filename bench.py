@@ -8,8 +8,9 @@ HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
 Printed: one JSON line with the step throughput, a roofline object for the dominant kernel (the
 fused forward, timed alone with HIP events on the stream it runs on), the backward of the QAT
 workload (B=1, H=16, N=8192, d=128) measured the same way, the forward with the exp-free EFQ
-probability codes, the cache forward on a decode batch and a chunked-prefill step, and the CPU
-oracle timed on a bounded sample of the same workload.
+probability codes, the forward on the causal LLM and GQA-prefill workloads, the cache forward on
+a decode batch and a chunked-prefill step, and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 import argparse
@@ -165,6 +166,31 @@ def bench_backward(args, torch, ops, W):
     t_roof = fp4 / (PEAK_FP4_TFLOPS * 1e9) + bf16 / (PEAK_BF16_TFLOPS * 1e9)
     return {"workload": w.name, "ms": ms, "fp4_flops": fp4, "bf16_flops": bf16,
             "tflops_total": (fp4 + bf16) / ms / 1e9, "roofline_ms": t_roof, "frac": t_roof / ms}
+
+
+def bench_forward_configs(args, torch, ops, W):
+    """The forward alone on the other forward workloads (causal LLM shape, GQA prefill), seeded
+    inputs, HIP events on its stream; flops count the visible (query, key) pairs, 4 d each."""
+    out = {}
+    for name in ("llm_causal_b2h16n4096d128", "gqa_causal_b1hq32hkv8n16384d128"):
+        w = W.WORKLOADS[name]
+        x = gen_inputs(w, ["q", "k", "v"])
+        dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
+        del x
+        qq = ops.attn_fp4_quantize(dev["q"], 0)
+        kq = ops.attn_fp4_quantize(dev["k"], 0)
+        vq = ops.attn_fp4_quantize(dev["v"], 1)
+        del dev
+        o, m, l = ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal)
+        fn = lambda: ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal, o=o, m=m, l=l)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ms = time_region(fn, max(5, args.steps), torch.cuda.current_stream())
+        pairs = w.B * w.Hq * (w.N * (w.N + 1) // 2 if w.causal else w.N * w.N)
+        tf = 4.0 * w.d * pairs / ms / 1e9
+        out[name] = {"ms": ms, "visible_pairs": pairs, "tflops": tf, "frac_mfma": tf / PEAK_FP4_TFLOPS}
+    return out
 
 
 def bench_kvcache(args, torch, ops, W, only=None):
@@ -348,6 +374,8 @@ def main():
     if not args.no_backward:
         result["backward"] = bench_backward(args, torch, ops, W)
         log("backward", result["backward"])
+    result["forward_configs"] = bench_forward_configs(args, torch, ops, W)
+    log("forward_configs", result["forward_configs"])
     result["kvcache"] = bench_kvcache(args, torch, ops, W)
     log("kvcache", result["kvcache"])
     if not args.no_cpu_baseline:

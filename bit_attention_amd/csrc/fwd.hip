@@ -114,9 +114,21 @@ fwd_kernel(FwdParams p) {
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
   const int64_t sp = SPLIT ? id % nsp : 0;        // key-tile range (split forward)
   id = SPLIT ? id / nsp : id;
-  const int64_t bh = id / nqt;                    // (b, query head), cache forward: (b, KV head)
+  int64_t bh = id / nqt;                          // (b, query head), cache forward: (b, KV head)
   int64_t qt = id - bh * nqt;
-  if (CAUSAL && !SPLIT) qt = nqt - 1 - qt;        // longest rows first
+  if (CAUSAL && !SPLIT) {
+    // longest rows first across all the heads of an XCD (query-tile major, heads interleaved), so
+    // that the workgroups left at the end are the short ones; the heads of an XCD stay together
+    const int64_t nbh = total / nqt;
+    if ((total & 7) == 0 && (nbh & 7) == 0) {
+      const int64_t hp = nbh >> 3;                // heads per XCD
+      const int64_t x = id / (total >> 3), j = id - x * (total >> 3);
+      bh = x * hp + j % hp;
+      qt = nqt - 1 - j / hp;
+    } else {
+      qt = nqt - 1 - qt;
+    }
+  }
   int64_t b, g, qrow;                             // qrow: the lane's row in [B, Hq, Nq] order
   int64_t NK;                                     // key rows per KV head in memory
   // last visible key of the lane's row, of the wave's first and last rows, of the workgroup's

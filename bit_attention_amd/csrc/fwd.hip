@@ -12,9 +12,16 @@
 //
 // gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
 // K^/V^ tile through LDS (four stages filled by direct global-to-LDS loads three tiles ahead;
-// one barrier per tile).  The
-// kernel is bound by the vector ALU (exp, E2M1 conversion, max), so it is shaped for three waves
-// per SIMD: while one wave waits on the matrix core or LDS, the others keep the VALU busy.
+// one barrier per tile).  On gfx950 the matrix core and the vector ALU barely overlap, so a tile
+// costs about the sum of its MFMA time and its VALU time (exp, E2M1 conversion, max, FMA); the
+// kernel is shaped for three waves per SIMD, which measured best, and keeps everything else (tile
+// loads, LDS reads, barriers) under that sum.
+//
+// The same kernel serves the cache forward (KV: new rows against a quantized key/value cache,
+// bottom-right causal, per-sequence lengths, query heads of a GQA group packed into the waves) and
+// the middle pass of its split form (SPLIT: one range of key tiles per workgroup).  The split form's
+// other passes follow the kernel: kv_max_kernel (each range's largest visible score) and
+// kv_merge_kernel (the ranges' partial results into O, m, l).
 //  * S is computed transposed, S^T = K^ Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = K^ rows
 //    from LDS, B = the wave's Q^ held in registers for the whole kernel).  The 64 K^ rows of a
 //    tile are staged with a permutation of the keys (slot_key) chosen so that, in the output

@@ -154,8 +154,9 @@ int32_t attn_fp4_fwd(const attn_fp4_fwd_args* args, void* stream);
  *   k_codes   [B, Hkv, Nk, d/2]  k_scales [B, Hkv, Nk, d/32] (axis 0)
  *   v_codes   [B, Hkv, Nk/32, d, 16]  v_scales [B, Hkv, Nk/32, d]
  *             (axis 1 over the cache's whole capacity Nk, block-major)
- *   seqlens_k int32 [B] device array: valid cache length L_b of sequence
- *             b (values are clamped to [0, Nk]); NULL means L_b = Nk.
+ *   seqlens_k int32 [B] device array, 4-byte aligned: valid cache length
+ *             L_b of sequence b (values are clamped to [0, Nk]); NULL means
+ *             L_b = Nk.
  *   o bf16 [B, Hq, Nq, d]; m, l fp32 [B, Hq, Nq] (outputs, as attn_fp4_fwd)
  * The Nq new rows are the last Nq positions of each sequence: their keys
  * and values are already in the cache, and new row i sits at position

@@ -13,12 +13,13 @@
 // Kernels (one launch each, all on the caller's stream):
 //  1. rows: D, m log2(e) and 1/l per query row.
 //  2. transposes: bf16 copies of the dequantized operands in the layouts the bf16 MFMAs read
-//     (V^ as [N, d]; K^, Q^ and dO as [d, N]); FP4 * 2^e is exact in bf16.
-//  3. dK/dV: a workgroup owns 64 keys (two 32-key pairs of waves) and walks all query rows of the
+//     (V^ as [N, d]; K^, Q^ as [d, N]; FP4 * 2^e is exact in bf16), and dO^T [d, N] with each
+//     query's 1/l folded in (dO * (1/l) rounded to bf16 once).
+//  3. dK/dV: a workgroup owns 16W keys (32-key pairs of waves) and walks all query rows of the
 //     KV head's query heads in tiles of 64.  S^T and dP^T are computed with one lane per query so
 //     that the 32-key P blocks sit in one lane pair, P~ is requantized in registers exactly as in
-//     the forward, and A = P~/l and dS are passed through LDS in [key][query] order to feed the
-//     dV^T = dO^T A and dK^T = Q^T dS products.
+//     the forward, and P~ (exact in bf16; its 1/l rides on dO^T) and dS pass through LDS to feed
+//     the dV^T = (dO diag(1/l))^T P~ and dK^T = Q^T dS products.
 //  4. dQ: a workgroup owns 32W query rows and walks the keys in tiles of 64:
 //     dQ^T = K^T dS^T with dS^T taken straight from registers.  No atomics: dQ, dK, dV are each
 //     written once, so the backward is deterministic.
@@ -75,11 +76,13 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
 // 2. 64x64 tile transpose to bf16: src logical [batch][R][C] -> dst [batch][C][R].
 //    FP4: src = packed E2M1 codes with E8M0 scales along C (dequantized exactly), row-major
 //    ([R][C/2] and [R][C/32]) or, with BLOCK_MAJOR, the V^ layout ([C/32][R][16], [C/32][R]);
-//    otherwise src = bf16 [R][C].
+//    otherwise src = bf16 [R][C], each row multiplied by rscale[row] (when given) and rounded
+//    to bf16 once.
 template <bool FP4, bool BLOCK_MAJOR = false>
 __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __restrict__ src,
                                                             const uint8_t* __restrict__ scl,
-                                                            uint16_t* __restrict__ dst, int64_t R, int64_t C) {
+                                                            uint16_t* __restrict__ dst, int64_t R, int64_t C,
+                                                            const float* __restrict__ rscale = nullptr) {
   __shared__ uint16_t tile[64][66];
   const int tid = threadIdx.x;
   const int64_t bz = blockIdx.z;
@@ -108,7 +111,12 @@ __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __res
     } else {
       const uint4* s = reinterpret_cast<const uint4*>(src + (row * C + c0 + cq) * 2);
       const uint4 a = s[0], b = s[1];
-      const uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      if (rscale != nullptr) {
+        const float f = rscale[row];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ww[i] = pk_bf16(bf16_lo(ww[i]) * f, bf16_hi(ww[i]) * f);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         tile[r][cq + 2 * i] = (uint16_t)(ww[i] & 0xFFFF);
@@ -401,10 +409,9 @@ bwd_dkdv_kernel(BwdParams p) {
         uint32_t u = 0;
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q], pr[4 * q + 1], sc, 0);
         u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
-        const v2f a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 0);   // P~ (dequantized)
-        const v2f a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, sc, 1);
-        aw[2 * q] = pk_bf16(a0[0] * il, a0[1] * il);
-        aw[2 * q + 1] = pk_bf16(a1[0] * il, a1[1] * il);
+        // A = P~ itself (exact in bf16); the 1/l of its query is carried by the dO^T operand
+        aw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 0));
+        aw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 1));
         float ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ds[i] = pr[4 * q + i] * il * (dp[4 * q + i] - dd);
@@ -785,8 +792,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
                      dim3(256), 0, stream, p.k_codes, p.k_scales, p.kt, N, d);
   hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
                      dim3(256), 0, stream, p.q_codes, p.q_scales, p.qt, N, d);
+  // dO^T carries each query's 1/l: dV^T = dO^T diag(1/l) P~ with P~ exact in bf16
   hipLaunchKernelGGL(bwd_transpose_kernel<false>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
-                     dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d);
+                     dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d,
+                     (const float*)p.il);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.d == 128) return p.causal ? launch_main<128, true>(p, stream) : launch_main<128, false>(p, stream);

@@ -62,7 +62,7 @@ struct BwdParams {
   uint16_t* vb;     // V^ dequantized, bf16 [B, Hkv, N, d]
   uint16_t* kt;     // K^ dequantized and transposed, bf16 [B, Hkv, d, N]
   uint16_t* qt;     // Q^ dequantized and transposed, bf16 [B, Hq, d, N]
-  uint16_t* dot;    // dO transposed, bf16 [B, Hq, d, N]
+  uint16_t* dot;    // dO transposed, each query row times its 1/l, bf16 [B, Hq, d, N]
   int64_t B, Hq, Hkv, N, d;
   int causal;
   float c;          // softmax_scale * log2(e)

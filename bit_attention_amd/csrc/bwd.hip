@@ -677,7 +677,8 @@ bwd_dq_kernel(BwdParams p) {
         const v4i a = *reinterpret_cast<const v4i*>(base + L::VB + slot * 2 * D + 16 * (cc ^ swz_big(slot, D / 8)));
         dp = mfma_bf16(a, ob[s], dp);
       }
-      // dS = P (dP - D), P = exp2(s c - m log2 e) / l; register r holds key 64t + 32T + 16hi + r
+      // dS l = p (dP - D), p = exp2(s c - m log2 e): the row's 1/l is applied to the finished dQ
+      // row instead of to every pair; register r holds key 64t + 32T + 16hi + r
       if (CAUSAL && ((int64_t)t * 64 + 63 > qw)) {
         const int jrel = (int)(row - (int64_t)t * 64) - 32 * T - 16 * hi;
 #pragma unroll
@@ -687,8 +688,8 @@ bwd_dq_kernel(BwdParams p) {
       uint32_t dsw[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i], c, -mq)) * il;
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i + 1], c, -mq)) * il;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i], c, -mq));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * i + 1], c, -mq));
         dsw[i] = pk_bf16(p0 * (dp[2 * i] - dd), p1 * (dp[2 * i + 1] - dd));
       }
       // dQ^T += K^T dS^T: k-step s2 takes keys 32T + 16 hi + 8 s2 + [0, 8) (registers 8 s2..)
@@ -723,9 +724,9 @@ bwd_dq_kernel(BwdParams p) {
     step(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- store dQ = scale * dQ^T: lane holds query `row`, channels 32 ct + 8 a + 4 hi + [0,4) ----
+  // ---- store dQ = scale / l * dQ^T: lane holds query `row`, channels 32 ct + 8 a + 4 hi + [0,4) ----
   uint16_t* dqr = p.dq + (bh * N + row) * D;
-  const float sc = p.scale_nat;
+  const float sc = p.scale_nat * il;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

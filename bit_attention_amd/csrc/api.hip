@@ -220,9 +220,7 @@ int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
   p.dk = (uint16_t*)a->dk;
   p.dv = (uint16_t*)a->dv;
   uint8_t* w = (uint8_t*)a->workspace;
-  p.delta = (float*)(w + ws.delta);
-  p.mq = (float*)(w + ws.mq);
-  p.il = (float*)(w + ws.il);
+  p.rowc = (float*)(w + ws.rowc);
   p.vb = (uint16_t*)(w + ws.vb);
   p.kt = (uint16_t*)(w + ws.kt);
   p.qt = (uint16_t*)(w + ws.qt);

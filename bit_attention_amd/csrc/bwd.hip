@@ -24,6 +24,7 @@
 //     dQ^T = K^T dS^T with dS^T taken straight from registers.  No atomics: dQ, dK, dV are each
 //     written once, so the backward is deterministic.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -39,14 +40,23 @@ __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
 }
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------------------------------------
 // 1. per-row constants
 // 16 lanes per row; rows = B*Hq*N is a multiple of 16.
 __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ m,
-                                                       const float* __restrict__ l, float* __restrict__ delta,
-                                                       float* __restrict__ mq, float* __restrict__ il,
+                                                       const float* __restrict__ l, float* __restrict__ rowc,
                                                        int64_t rows, int d) {
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int sub = threadIdx.x & 15;
@@ -66,9 +76,7 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 8, 16);
   if (sub == 0) {
-    delta[r] = acc;
-    mq[r] = m[r] * kLog2e;
-    il[r] = 1.0f / l[r];
+    *reinterpret_cast<float4*>(rowc + 4 * r) = make_float4(m[r] * kLog2e, 1.0f / l[r], acc, 0.0f);
   }
 }
 
@@ -76,8 +84,8 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
 // 2. 64x64 tile transpose to bf16: src logical [batch][R][C] -> dst [batch][C][R].
 //    FP4: src = packed E2M1 codes with E8M0 scales along C (dequantized exactly), row-major
 //    ([R][C/2] and [R][C/32]) or, with BLOCK_MAJOR, the V^ layout ([C/32][R][16], [C/32][R]);
-//    otherwise src = bf16 [R][C], each row multiplied by rscale[row] (when given) and rounded
-//    to bf16 once.
+//    otherwise src = bf16 [R][C], each row multiplied by rscale[4 row] (when given: the 1/l entry
+//    of the per-row constants) and rounded to bf16 once.
 template <bool FP4, bool BLOCK_MAJOR = false>
 __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __restrict__ src,
                                                             const uint8_t* __restrict__ scl,
@@ -113,7 +121,7 @@ __global__ void __launch_bounds__(256) bwd_transpose_kernel(const uint8_t* __res
       const uint4 a = s[0], b = s[1];
       uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       if (rscale != nullptr) {
-        const float f = rscale[row];
+        const float f = rscale[4 * row];
 #pragma unroll
         for (int i = 0; i < 8; ++i) ww[i] = pk_bf16(bf16_lo(ww[i]) * f, bf16_hi(ww[i]) * f);
       }
@@ -180,8 +188,8 @@ struct DkdvLds {
   static constexpr int KEYS = 16 * W;                 // 32 keys per pair of waves
   static constexpr int QC = 0;                        // A: Q^ codes [64 q][D/2]
   static constexpr int QS = QC + 64 * D / 2;          // A: Q^ scales [64 q] dwords
-  static constexpr int ROWS = QS + 64 * 4;            // A: mq, il, D: 3 x [64] floats
-  static constexpr int DO = ROWS + 3 * 64 * 4;        // A: dO bf16 [64 q][D], swizzled chunks
+  static constexpr int ROWS = QS + 64 * 4;            // A: (mq, il, D, 0) [64 q] float4
+  static constexpr int DO = ROWS + 64 * 16;           // A: dO bf16 [64 q][D], swizzled chunks
   static constexpr int A_BYTES = DO + 64 * D * 2;
   static constexpr int DOT = 0;                       // B: dO^T bf16 [D][64 q], swizzled chunks
   static constexpr int QT = DOT + D * 64 * 2;         // B: Q^T bf16 [D][64 q], swizzled chunks
@@ -252,111 +260,120 @@ bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- staging jobs (one 64-lane LDS-DMA instruction each) ----
-  // group A: Q^ codes (1-KB pieces), dO (1-KB pieces), Q^ scales, mq, il, D; group B: dO^T, Q^T.
-  // The query heads of this KV head are contiguous, so one resource per tensor covers them; the
-  // tile's (head, row) offset goes in the scalar offset.
+  // group A: dO (1-KB pieces), Q^ codes (1-KB pieces), the Q^ scales and the per-row constants;
+  // group B: dO^T, Q^T.  Job j of a group is issued by wave j % W in slot j / W (the last job
+  // repeated where the list runs out: an identical rewrite).  A slot whose jobs are all of one kind
+  // is emitted without a branch, a mixed one with at most two wave-uniform compares.  The query
+  // heads of this KV head are contiguous, so one resource per tensor covers them; the tile's
+  // (head, row) offset goes in the scalar offset.
   constexpr int NQC = 64 * D / 2 / 1024, NDO = 64 * D * 2 / 1024;
-  constexpr int NA = NQC + NDO + 4, NB = 2 * (D * 64 * 2 / 1024);
+  constexpr int NA = NDO + NQC + 2, NB = 2 * (D * 64 * 2 / 1024);
   constexpr int JA = (NA + W - 1) / W, JB = (NB + W - 1) / W;
   const int64_t hq0 = b * p.Hq + g * group;       // first query head of this KV head
   const auto qc_rs = make_rsrc(p.q_codes + hq0 * N * (D / 2), group * N * (D / 2));
   const auto qs_rs = make_rsrc(p.q_scales + hq0 * N * (D / 32), group * N * (D / 32));
   const auto do_rs = make_rsrc(p.dout + hq0 * N * D, group * N * D * 2);
-  const auto mq_rs = make_rsrc(p.mq + hq0 * N, group * N * 4);
-  const auto il_rs = make_rsrc(p.il + hq0 * N, group * N * 4);
-  const auto dl_rs = make_rsrc(p.delta + hq0 * N, group * N * 4);
+  const auto rc_rs = make_rsrc(p.rowc + hq0 * N * 4, group * N * 16);
   const auto dot_rs = make_rsrc(p.dot + hq0 * D * N, group * D * N * 2);
   const auto qt_rs = make_rsrc(p.qt + hq0 * D * N, group * D * N * 2);
-  // kinds: 0 Q^ codes, 1 dO, 2 Q^ scales, 3 mq, 4 il, 5 D | 6 dO^T, 7 Q^T
-  auto kind_a = [](int j) constexpr { return j < NQC ? 0 : j < NQC + NDO ? 1 : 2 + (j - NQC - NDO); };
-  auto kind_b = [](int j) constexpr { return j < NB / 2 ? 6 : 7; };
+  // kinds: 0 dO, 1 Q^ codes, 2 Q^ scales, 3 row constants | 4 dO^T, 5 Q^T
+  auto kind_a = [](int j) constexpr { return j < NDO ? 0 : j < NDO + NQC ? 1 : j == NDO + NQC ? 2 : 3; };
+  auto kind_b = [](int j) constexpr { return j < NB / 2 ? 4 : 5; };
   auto goff_of = [&](int kind, int j) -> uint32_t {   // lane's global byte offset within the tile
-    if (kind == 0) return 16 * (64 * j + lane);
-    if (kind == 1) {
-      const int cidx = 64 * (j - NQC) + lane, q = cidx / RC, cc = (cidx % RC) ^ swz_big(q, RC);
+    if (kind == 0) {
+      const int cidx = 64 * j + lane, q = cidx / RC, cc = (cidx % RC) ^ swz_big(q, RC);
       return q * (D * 2) + 16 * cc;
     }
+    if (kind == 1) return 16 * (64 * (j - NDO) + lane);
     if (kind == 2) return lane * (D / 32);
-    if (kind <= 5) return 4 * lane;
-    const int cidx = 64 * (kind == 6 ? j : j - NB / 2) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
+    if (kind == 3) return 16 * lane;
+    const int cidx = 64 * (kind == 4 ? j : j - NB / 2) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
     return (uint32_t)ch * (uint32_t)(N * 2) + 16 * cc;
   };
   auto dst_of = [](int kind, int j) -> int {   // within the group's buffer
-    return kind == 0 ? L::QC + 1024 * j : kind == 1 ? L::DO + 1024 * (j - NQC) : kind == 2 ? L::QS
-         : kind <= 5 ? L::ROWS + 256 * (kind - 3) : kind == 6 ? L::DOT + 1024 * j : L::QT + 1024 * (j - NB / 2);
+    return kind == 0 ? L::DO + 1024 * j : kind == 1 ? L::QC + 1024 * (j - NDO) : kind == 2 ? L::QS : kind == 3 ? L::ROWS
+         : kind == 4 ? L::DOT + 1024 * j : L::QT + 1024 * (j - NB / 2);
   };
-  constexpr bool PRE_A = JA <= 6, PRE_B = JB <= 6;
-  uint32_t goff_a[PRE_A ? JA : 1], goff_b[PRE_B ? JB : 1];
-  if constexpr (PRE_A) {
+  uint32_t goff_a[JA], goff_b[JB];
 #pragma unroll
-    for (int i = 0; i < JA; ++i) { const int j = min(wave + W * i, NA - 1); goff_a[i] = goff_of(kind_a(j), j); }
-  }
-  if constexpr (PRE_B) {
+  for (int i = 0; i < JA; ++i) { const int j = min(wave + W * i, NA - 1); goff_a[i] = goff_of(kind_a(j), j); }
 #pragma unroll
-    for (int i = 0; i < JB; ++i) { const int j = min(wave + W * i, NB - 1); goff_b[i] = goff_of(kind_b(j), j); }
-  }
-  // row offsets of query tile (hh, q0) in elements: along the rows of [head][N] and of [head][D][N]
-  auto issue = [&](int kind, int j, uint32_t goff, int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
-    const int base = kind <= 5 ? L::A0 + buf * L::A_BYTES : L::B0 + buf * L::B_BYTES;
+  for (int i = 0; i < JB; ++i) { const int j = min(wave + W * i, NB - 1); goff_b[i] = goff_of(kind_b(j), j); }
+  // one job of a compile-time kind; r = the tile's first row of [head][N], tcol = its first element
+  // of [head][D][N] (both wave-uniform)
+  auto issue_kind = [&](auto kc, int j, uint32_t goff, int r, int tcol, int buf) __attribute__((always_inline)) {
+    constexpr int kind = decltype(kc)::value;
+    const int base = kind <= 3 ? L::A0 + buf * L::A_BYTES : L::B0 + buf * L::B_BYTES;
     auto* dst = (__attribute__((address_space(3))) void*)(smem + base + dst_of(kind, j));   // LDS-DMA target
-    const int r = __builtin_amdgcn_readfirstlane((int)(hh * N + q0));                  // row of [head][N]
-    const int tcol = __builtin_amdgcn_readfirstlane((int)(hh * D * N + q0));          // element of [head][D][N]
-    switch (kind) {
-      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(qc_rs, dst, 16, (int)goff, r * (D / 2), 0, 0); break;
-      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(do_rs, dst, 16, (int)goff, r * (D * 2), 0, 0); break;
-      case 2:
-        if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 4, (int)goff, r * (D / 32), 0, 0);
-        else __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 2, (int)goff, r * (D / 32), 0, 0);
-        break;
-      case 3: __builtin_amdgcn_raw_ptr_buffer_load_lds(mq_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
-      case 4: __builtin_amdgcn_raw_ptr_buffer_load_lds(il_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
-      case 5: __builtin_amdgcn_raw_ptr_buffer_load_lds(dl_rs, dst, 4, (int)goff, r * 4, 0, 0); break;
-      case 6: __builtin_amdgcn_raw_ptr_buffer_load_lds(dot_rs, dst, 16, (int)goff, tcol * 2, 0, 0); break;
-      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(qt_rs, dst, 16, (int)goff, tcol * 2, 0, 0); break;
-    }
+    if constexpr (kind == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(do_rs, dst, 16, (int)goff, r * (D * 2), 0, 0);
+    else if constexpr (kind == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(qc_rs, dst, 16, (int)goff, r * (D / 2), 0, 0);
+    else if constexpr (kind == 2) {   // d/32 bytes per row
+      if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 4, (int)goff, r * (D / 32), 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 2, (int)goff, r * (D / 32), 0, 0);
+    } else if constexpr (kind == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rc_rs, dst, 16, (int)goff, r * 16, 0, 0);
+    else if constexpr (kind == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(dot_rs, dst, 16, (int)goff, tcol * 2, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(qt_rs, dst, 16, (int)goff, tcol * 2, 0, 0);
   };
-  auto issue_a = [&](int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < JA; ++i) {
+  // slot i of a group: the kinds of its jobs span [klo, khi] (known at compile time)
+  auto issue_slot = [&](auto klo_c, auto khi_c, int kind, int j, uint32_t goff, int r, int tcol, int buf)
+      __attribute__((always_inline)) {
+    constexpr int klo = decltype(klo_c)::value, khi = decltype(khi_c)::value;
+    static_assert(khi - klo <= 2, "kinds per slot");
+    using K0 = std::integral_constant<int, klo>;
+    using K1 = std::integral_constant<int, (klo + 1 < khi ? klo + 1 : khi)>;
+    using K2 = std::integral_constant<int, khi>;
+    if constexpr (klo == khi) issue_kind(K0{}, j, goff, r, tcol, buf);
+    else if (kind == klo) issue_kind(K0{}, j, goff, r, tcol, buf);
+    else if (khi - klo >= 2 && kind == klo + 1) issue_kind(K1{}, j, goff, r, tcol, buf);
+    else issue_kind(K2{}, j, goff, r, tcol, buf);
+  };
+  auto issue_a = [&](int r, int buf) __attribute__((always_inline)) {
+    static_for<JA>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int jlo = W * i < NA - 1 ? W * i : NA - 1, jhi = W * i + W - 1 < NA - 1 ? W * i + W - 1 : NA - 1;
       const int j = min(wave + W * i, NA - 1);
-      uint32_t goff;
-      if constexpr (PRE_A) goff = goff_a[PRE_A ? i : 0];
-      else goff = goff_of(kind_a(j), j);
-      issue(kind_a(j), j, goff, hh, q0, buf);
-    }
+      issue_slot(std::integral_constant<int, kind_a(jlo)>{}, std::integral_constant<int, kind_a(jhi)>{}, kind_a(j), j,
+                 goff_a[i], r, 0, buf);
+    });
   };
-  auto issue_b = [&](int64_t hh, int64_t q0, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < JB; ++i) {
+  auto issue_b = [&](int tcol, int buf) __attribute__((always_inline)) {
+    static_for<JB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int jlo = W * i < NB - 1 ? W * i : NB - 1, jhi = W * i + W - 1 < NB - 1 ? W * i + W - 1 : NB - 1;
       const int j = min(wave + W * i, NB - 1);
-      uint32_t goff;
-      if constexpr (PRE_B) goff = goff_b[PRE_B ? i : 0];
-      else goff = goff_of(kind_b(j), j);
-      issue(kind_b(j), j, goff, hh, q0, buf);
-    }
+      issue_slot(std::integral_constant<int, kind_b(jlo)>{}, std::integral_constant<int, kind_b(jhi)>{}, kind_b(j), j,
+                 goff_b[i], 0, tcol, buf);
+    });
   };
 
   // ---- tiles: the query heads of the group, and per head the query tiles that see any key ----
-  const int64_t j_first = CAUSAL ? k0 / 64 : 0;   // query tiles below the keys see none of them
-  const int64_t nj = N / 64 - j_first;
-  const int64_t ntile = group * nj;
-  // query tile n as (head of the group hh, tile jj): the tiles of a head are consecutive
-  auto next = [&](int64_t& h_, int64_t& j_) __attribute__((always_inline)) {
+  // (all wave-uniform 32-bit scalars: group * D * N * 2 < 2^31 is checked at the boundary)
+  const int j_first = CAUSAL ? (int)(k0 / 64) : 0;   // query tiles below the keys see none of them
+  const int nj = (int)(N / 64) - j_first;
+  const int ntile = (int)group * nj;
+  // query tile n as (head of the group, tile j of the head): the tiles of a head are consecutive
+  auto next = [&](int& h_, int& j_) __attribute__((always_inline)) {
     if (++j_ == nj) { j_ = 0; ++h_; }
   };
-  int64_t hh = 0, jj = 0;                          // tile n
-  int64_t hn = 0, jn = 0;                          // tile n + 1
+  auto row_of = [&](int h_, int j_) __attribute__((always_inline)) {        // first row of [head][N]
+    return __builtin_amdgcn_readfirstlane(h_ * (int)N + (j_first + j_) * 64);
+  };
+  auto tcol_of = [&](int h_, int j_) __attribute__((always_inline)) {       // first element of [head][D][N]
+    return __builtin_amdgcn_readfirstlane(h_ * D * (int)N + (j_first + j_) * 64);
+  };
+  int jj = 0;                                      // tile n (its row within the head)
+  int hn = 0, jn = 0;                              // tile n + 1
   next(hn, jn);
-  issue_a(0, j_first * 64, 0);
-  issue_b(0, j_first * 64, 0);
-  if (ntile > 1) issue_a(hn, (j_first + jn) * 64, 1);
+  issue_a(row_of(0, 0), 0);
+  issue_b(tcol_of(0, 0), 0);
+  if (ntile > 1) issue_a(row_of(hn, jn), 1);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // one tile; the buffer index is a compile-time constant (the loop below is unrolled by two) so
   // that the compiler sees which LDS bytes the direct loads write and adds no waits of its own
-  auto tile = [&](auto bufc, int64_t n) __attribute__((always_inline)) {
+  auto tile = [&](auto bufc, int n) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int64_t q0 = (j_first + jj) * 64;
-    int64_t h2 = hn, j2 = jn;                       // tile n + 2
+    const int q0 = (j_first + jj) * 64;
+    int h2 = hn, j2 = jn;                           // tile n + 2
     next(h2, j2);
     const uint8_t* sa = smem + L::A0 + buf * L::A_BYTES;
     const uint8_t* sb = smem + L::B0 + buf * L::B_BYTES;
@@ -383,9 +400,8 @@ bwd_dkdv_kernel(BwdParams p) {
         const v4i bo = *reinterpret_cast<const v4i*>(sa + L::DO + ql * 2 * D + 16 * (cc ^ swz_big(ql, RC)));
         dp = mfma_bf16(va[s], bo, dp);
       }
-      const float mq = reinterpret_cast<const float*>(sa + L::ROWS)[ql];
-      const float il = reinterpret_cast<const float*>(sa + L::ROWS)[64 + ql];
-      const float dd = reinterpret_cast<const float*>(sa + L::ROWS)[128 + ql];
+      const float4 rc = reinterpret_cast<const float4*>(sa + L::ROWS)[ql];
+      const float mq = rc.x, il = rc.y, dd = rc.z;
       // register r holds key kp + 16 hi + r
       if (CAUSAL) {
         const int jrel = (int)(qrow - kp) - 16 * hi;
@@ -442,8 +458,8 @@ bwd_dkdv_kernel(BwdParams p) {
       };
       // group A of tile n + 2 (into this tile's A buffer, read by the elementwise phase that has
       // ended) and group B of tile n + 1 (into the other B buffer, free since tile n - 1)
-      if (n + 2 < ntile) issue_a(h2, (j_first + j2) * 64, buf);
-      if (n + 1 < ntile) issue_b(hn, (j_first + jn) * 64, 1 - buf);
+      if (n + 2 < ntile) issue_a(row_of(h2, j2), buf);
+      if (n + 1 < ntile) issue_b(tcol_of(hn, jn), 1 - buf);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int qa = 16 * s + 8 * hi + (gi >> 2);   // rows of the two transposing loads: qa, qa + 4
@@ -464,14 +480,18 @@ bwd_dkdv_kernel(BwdParams p) {
       }
     }
     // the scratch and this tile's B buffer are free (group A of tile n + 1 landed before the
-    // products); the loads issued above stay in flight
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    hh = hn;
+    // products); the loads issued above stay in flight.  The accumulators are operands so that
+    // the products stay on this side of the barrier (the register allocator otherwise copies
+    // them between the two unrolled tiles).
+    if constexpr (CT == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : "+v"(dv[0]), "+v"(dv[1]), "+v"(dk[0]), "+v"(dk[CT - 1]) :: "memory");
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : "+v"(dv[0]), "+v"(dk[0]) :: "memory");
     jj = jn;
     hn = h2;
     jn = j2;
   };
-  for (int64_t n = 0; n < ntile; n += 2) {
+  for (int n = 0; n < ntile; n += 2) {
     tile(std::integral_constant<int, 0>{}, n);
     if (n + 1 >= ntile) break;
     tile(std::integral_constant<int, 1>{}, n + 1);
@@ -551,7 +571,8 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < DS_STEPS; ++s) ob[s] = *reinterpret_cast<const v4i*>(orow + 16 * s + 8 * hi);
   }
-  const float mq = p.mq[bh * N + row], il = p.il[bh * N + row], dd = p.delta[bh * N + row];
+  const float4 rc = reinterpret_cast<const float4*>(p.rowc)[bh * N + row];
+  const float mq = rc.x, il = rc.y, dd = rc.z;
 
   v16f acc[CT];
 #pragma unroll
@@ -766,11 +787,8 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
 
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
   BwdWorkspace w;
-  const int64_t rows = align256(B * Hq * N * 4);
-  w.delta = 0;
-  w.mq = w.delta + rows;
-  w.il = w.mq + rows;
-  w.vb = w.il + rows;
+  w.rowc = 0;
+  w.vb = w.rowc + align256(B * Hq * N * 16);
   w.kt = w.vb + align256(B * Hkv * N * d * 2);
   w.qt = w.kt + align256(B * Hkv * N * d * 2);
   w.dot = w.qt + align256(B * Hq * N * d * 2);
@@ -781,7 +799,7 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int64_t rows = p.B * p.Hq * p.N;
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p.o, p.dout, p.m,
-                     p.l, p.delta, p.mq, p.il, rows, (int)p.d);
+                     p.l, p.rowc, rows, (int)p.d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t d = p.d, N = p.N;
@@ -796,7 +814,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   // dO^T carries each query's 1/l: dV^T = dO^T diag(1/l) P~ with P~ exact in bf16
   hipLaunchKernelGGL(bwd_transpose_kernel<false>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
                      dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d,
-                     (const float*)p.il);
+                     (const float*)p.rowc + 1);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.d == 128) return p.causal ? launch_main<128, true>(p, stream) : launch_main<128, false>(p, stream);

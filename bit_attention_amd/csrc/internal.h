@@ -56,9 +56,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   // workspace (carved by the host layer, see BwdWorkspace)
-  float* delta;     // D = rowsum(dO * O), [B, Hq, N]
-  float* mq;        // m * log2(e), [B, Hq, N]
-  float* il;        // 1 / l, [B, Hq, N]
+  float* rowc;      // per query row (m * log2(e), 1 / l, D = rowsum(dO * O), 0), [B, Hq, N, 4]
   uint16_t* vb;     // V^ dequantized, bf16 [B, Hkv, N, d]
   uint16_t* kt;     // K^ dequantized and transposed, bf16 [B, Hkv, d, N]
   uint16_t* qt;     // Q^ dequantized and transposed, bf16 [B, Hq, d, N]
@@ -71,7 +69,7 @@ struct BwdParams {
 
 // Byte offsets of the backward's workspace regions (each 256-byte aligned).
 struct BwdWorkspace {
-  int64_t delta, mq, il, vb, kt, qt, dot, total;
+  int64_t rowc, vb, kt, qt, dot, total;
 };
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
 

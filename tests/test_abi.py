@@ -80,7 +80,7 @@ def test_host_validation_rejects_before_launch():
     a = ops.FwdKvcacheArgs(p, p, p, p, p, p, None, p, p, p, None, 0, 1, 1, 1, 1, big, 128, 0, 0.0, 0)
     assert L.attn_fp4_fwd_kvcache(ctypes.byref(a), None) == 3
     # rows: 3 x [B*Hq*N] fp32; bf16 copies: V^ and K^T per KV head, Q^T and dO^T per query head
-    assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 3 * 1024 + 4 * (2 * 128 * 128 * 2)
+    assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 128, 128) == 2 * 128 * 16 + 4 * (2 * 128 * 128 * 2)
     assert L.attn_fp4_bwd_workspace_bytes(1, 2, 2, 100, 128) < 0
     b = ops.BwdArgs(p, p, p, p, p, p, p, p, p, p, p, p, p, None, 0, 1, 2, 2, 128, 128, 0, 0.0)
     assert L.attn_fp4_bwd_recompute(ctypes.byref(b), None) == 5   # workspace missing

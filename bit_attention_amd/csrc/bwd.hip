@@ -50,6 +50,13 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
+// XOR swizzle of the 16-byte chunks of an FP4 code row in LDS (64 B = 4 chunks at d = 128, 32 B =
+// 2 chunks at d = 64), so that 16 lanes reading one logical chunk of 16 consecutive rows hit 16
+// distinct 4-bank groups.
+__device__ __forceinline__ int swz_code(int row, int nchunks) {
+  return nchunks == 4 ? (((row >> 1) ^ (row >> 2)) & 3) : ((row >> 3) & 1);
+}
+
 // ---------------------------------------------------------------------------------------------
 // 1. per-row constants
 // 16 lanes per row; rows = B*Hq*N is a multiple of 16.
@@ -57,7 +64,11 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ m,
                                                        const float* __restrict__ l, float* __restrict__ rowc,
-                                                       int64_t rows, int d) {
+                                                       int64_t rows, int d,
+                                                       const uint8_t* __restrict__ q_codes = nullptr,
+                                                       const uint8_t* __restrict__ q_scales = nullptr,
+                                                       uint16_t* __restrict__ qb = nullptr,
+                                                       uint16_t* __restrict__ dos = nullptr) {
   const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int sub = threadIdx.x & 15;
   if (r >= rows) return;
@@ -75,8 +86,31 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 8, 16);
-  if (sub == 0) {
-    *reinterpret_cast<float4*>(rowc + 4 * r) = make_float4(m[r] * kLog2e, 1.0f / l[r], acc, 0.0f);
+  const float il = 1.0f / l[r];
+  if (sub == 0) *reinterpret_cast<float4*>(rowc + 4 * r) = make_float4(m[r] * kLog2e, il, acc, acc * il);
+  if (dos != nullptr) {                         // dO / l, rounded to bf16 once (d = 128)
+    const uint4 gv = *reinterpret_cast<const uint4*>(grow);
+    const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint4 out;
+    out.x = pk_bf16(bf16_lo(w[0]) * il, bf16_hi(w[0]) * il);
+    out.y = pk_bf16(bf16_lo(w[1]) * il, bf16_hi(w[1]) * il);
+    out.z = pk_bf16(bf16_lo(w[2]) * il, bf16_hi(w[2]) * il);
+    out.w = pk_bf16(bf16_lo(w[3]) * il, bf16_hi(w[3]) * il);
+    *reinterpret_cast<uint4*>(dos + r * d + sub * 8) = out;
+  }
+  if (qb != nullptr) {                          // Q^ dequantized to bf16 (exact), d = 128
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(q_codes + r * (d / 2) + sub * 4);
+    const int e = (int)q_scales[r * (d / 32) + sub / 4] - 127;
+    const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+    const v2f bb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+    const v2f cc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+    const v2f dd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+    const float v[8] = {a[0], a[1], bb[0], bb[1], cc[0], cc[1], dd[0], dd[1]};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = __float_as_uint(__builtin_ldexpf(v[i], e)) >> 16;   // exact in bf16
+    *reinterpret_cast<uint4*>(qb + r * d + sub * 8) =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
   }
 }
 
@@ -220,6 +254,7 @@ bwd_dkdv_kernel(BwdParams p) {
   constexpr int CH = D / 2;               // channels accumulated per wave
   constexpr int CT = CH / 32;             // 32-channel tiles per wave
   constexpr int RC = D / 8;               // 16-B chunks per dO row
+  constexpr int KCH = D / 32;             // 16-B chunks per Q^ code row
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
 
   const int tid = threadIdx.x;
@@ -284,7 +319,10 @@ bwd_dkdv_kernel(BwdParams p) {
       const int cidx = 64 * j + lane, q = cidx / RC, cc = (cidx % RC) ^ swz_big(q, RC);
       return q * (D * 2) + 16 * cc;
     }
-    if (kind == 1) return 16 * (64 * (j - NDO) + lane);
+    if (kind == 1) {                                   // Q^ codes, chunks swizzled by row
+      const int cidx = 64 * (j - NDO) + lane, q = cidx / KCH, cc = (cidx % KCH) ^ swz_code(q, KCH);
+      return q * (D / 2) + 16 * cc;
+    }
     if (kind == 2) return lane * (D / 32);
     if (kind == 3) return 16 * lane;
     const int cidx = 64 * (kind == 4 ? j : j - NB / 2) + lane, ch = cidx >> 3, cc = (cidx & 7) ^ swz_big(ch, 8);
@@ -384,14 +422,15 @@ bwd_dkdv_kernel(BwdParams p) {
       const int64_t qrow = q0 + ql;
       // S^T = K^ Q^T (FP4)
       const uint8_t* qcl = sa + L::QC + ql * (D / 2);
+      const int qx = swz_code(ql, KCH);
       const uint32_t qsw = *reinterpret_cast<const uint32_t*>(sa + L::QS + 4 * ql);
       const int qsc = (int)(qsw >> (8 * hi));
       v16f st = v16f{};
-      st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi)),
+      st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[0]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * (hi ^ qx))),
                                                           st, 4, 4, 0, ksc, 0, qsc);
       if (KS_STEPS == 2)
         st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            widen(ka[KS_STEPS - 1]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * hi + 32)), st, 4, 4, 2, ksc, 2, qsc);
+            widen(ka[KS_STEPS - 1]), widen(*reinterpret_cast<const v4i*>(qcl + 16 * ((hi + 2) ^ qx))), st, 4, 4, 2, ksc, 2, qsc);
       // dP^T = V^ dO^T (bf16)
       v16f dp = v16f{};
 #pragma unroll
@@ -515,6 +554,396 @@ bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// 3b. dK / dV at d = 128 with producer and consumer waves (N % 128 = 0).  A workgroup of eight
+// waves owns 128 keys.  In each step waves 0-3 (one per SIMD) run the elementwise phase of query
+// tile n while waves 4-7 run the products of tile n - 1, so that every SIMD holds one VALU-heavy
+// and one matrix-core-heavy wave at all times; one barrier per step.
+//  * elementwise wave e: keys 64 (e / 2) + [0, 64) as two 32-key P blocks, queries 32 (e % 2) +
+//    [0, 32).  S^T = K^ Q^T (FP4) and dP^T / l = V^ (dO / l)^T (bf16), one lane per query as in
+//    the forward; P~ requantized in registers; dS = p (dP / l - D / l).  P~ (exact in bf16) and
+//    dS go to a query-major scratch [64 q][128 keys].
+//  * product wave c: keys 64 (c / 2) + [0, 64), channels 64 (c % 2) + [0, 64):
+//    dV^T += (dO / l)^T P~ and dK^T += Q^T dS over the tile's 64 queries.  All operands come from
+//    row-major tiles through the transposing LDS load (ds_read_b64_tr_b16).
+// LDS (163584 bytes): three group-A buffers (Q^ codes and scales, row constants, dO / l; a tile's
+// buffer is read by the elementwise phase in one step and by the products in the next), two Q^
+// (bf16) buffers and two scratch buffers.  Every LDS access of the two phases is an asm statement
+// that waits for its own loads, so buffers are picked at run time without the compiler waiting
+// for the direct loads in flight; the barrier of each step waits for everything.
+struct DkdvWsLds {
+  static constexpr int QC = 0;                  // Q^ codes [64 q][64 B], chunks swizzled (swz_code)
+  static constexpr int QS = QC + 4096;          // Q^ scales [64 q] dwords
+  static constexpr int ROWS = QS + 256;         // (mq, il, D, D / l) [64 q] float4
+  static constexpr int DOS = ROWS + 1024;       // dO / l bf16 [64 q][128], chunks swizzled (x16)
+  static constexpr int A_BYTES = DOS + 16384;
+  static constexpr int B_BYTES = 16384;         // Q^ bf16 [64 q][128], chunks swizzled (x16)
+  static constexpr int S_BYTES = 32768;         // P~ then dS, bf16 [64 q][128 keys] each (x16)
+  static constexpr int A0 = 0, B0 = 3 * A_BYTES, S0 = B0 + 2 * B_BYTES;
+  static constexpr int BYTES = S0 + 2 * S_BYTES;
+};
+static_assert(DkdvWsLds::BYTES <= 163840, "LDS");
+
+// 16-byte chunk swizzle of 256-byte rows: a permutation of the 16 chunks within every 16 rows, so
+// that 16 consecutive rows read at one logical chunk (the MFMA operand loads), and 4 consecutive
+// rows read at two adjacent chunks (the transposing loads, 32 lanes), both spread over all banks.
+__device__ __forceinline__ int x16(int q) { return ((q & 3) << 2) | ((q >> 2) & 3); }
+__device__ __forceinline__ int x16_off(int q, int c) { return q * 256 + 16 * (c ^ x16(q)); }
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_ws_kernel(BwdParams p) {
+  using L = DkdvWsLds;
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int gi = lane & 15, gh = (lane >> 4) & 1;
+  const int r4 = wave & 3;
+  const int kh = r4 >> 1;                          // 64-key half of the workgroup's keys
+
+  const int64_t N = p.N;
+  const int64_t nkt = N / 128;
+  const int64_t bg = blockIdx.x / nkt;            // b * Hkv + g
+  const int64_t k0 = (blockIdx.x - bg * nkt) * 128;
+  const int64_t b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int64_t group = p.Hq / p.Hkv;
+  const float c = p.c;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+
+  // ---- staging jobs (one 64-lane LDS-DMA instruction each) ----
+  // group A: dO / l (1-KB pieces), Q^ codes (1-KB pieces), Q^ scales, row constants; group B: Q^
+  // bf16.  Job j of a group is issued by wave j % 8 in slot j / 8 (the last job repeated where the
+  // list runs out).  The query heads of this KV head are contiguous, so one resource per tensor
+  // covers them; the tile's first row goes in the scalar offset.
+  constexpr int NA = 16 + 4 + 2, NB = 16;
+  constexpr int JA = (NA + 7) / 8, JB = NB / 8;
+  const int64_t hq0 = b * p.Hq + g * group;       // first query head of this KV head
+  const auto qc_rs = make_rsrc(p.q_codes + hq0 * N * (D / 2), group * N * (D / 2));
+  const auto qs_rs = make_rsrc(p.q_scales + hq0 * N * (D / 32), group * N * (D / 32));
+  const auto rc_rs = make_rsrc(p.rowc + hq0 * N * 4, group * N * 16);
+  const auto ds_rs = make_rsrc(p.dos + hq0 * N * D, group * N * D * 2);
+  const auto qb_rs = make_rsrc(p.qb + hq0 * N * D, group * N * D * 2);
+  // kinds: 0 dO / l, 1 Q^ codes, 2 Q^ scales, 3 row constants | 4 Q^ bf16
+  auto kind_a = [](int j) constexpr { return j < 16 ? 0 : j < 20 ? 1 : j == 20 ? 2 : 3; };
+  auto goff_of = [&](int kind, int j) -> uint32_t {   // lane's global byte offset within the tile
+    if (kind == 0 || kind == 4) {
+      const int pos = 64 * j + lane, q = pos >> 4;
+      return q * 256 + 16 * ((pos & 15) ^ x16(q));
+    }
+    if (kind == 1) {
+      const int pos = 64 * (j - 16) + lane, q = pos >> 2;
+      return q * 64 + 16 * ((pos & 3) ^ swz_code(q, 4));
+    }
+    return kind == 2 ? 4 * lane : 16 * lane;
+  };
+  auto dst_of = [](int kind, int j) -> int {
+    return kind == 0 ? L::DOS + 1024 * j : kind == 1 ? L::QC + 1024 * (j - 16) : kind == 2 ? L::QS
+         : kind == 3 ? L::ROWS : 1024 * j;
+  };
+  uint32_t goff_a[JA], goff_b[JB];
+#pragma unroll
+  for (int i = 0; i < JA; ++i) { const int j = min(wave + 8 * i, NA - 1); goff_a[i] = goff_of(kind_a(j), j); }
+#pragma unroll
+  for (int i = 0; i < JB; ++i) goff_b[i] = goff_of(4, wave + 8 * i);
+  auto issue_kind = [&](auto kc, int j, uint32_t goff, int r, int dst_base) __attribute__((always_inline)) {
+    constexpr int kind = decltype(kc)::value;
+    auto* dst = (__attribute__((address_space(3))) void*)(smem + dst_base + dst_of(kind, j));   // LDS-DMA target
+    if constexpr (kind == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(ds_rs, dst, 16, (int)goff, r * (D * 2), 0, 0);
+    else if constexpr (kind == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(qc_rs, dst, 16, (int)goff, r * (D / 2), 0, 0);
+    else if constexpr (kind == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(qs_rs, dst, 4, (int)goff, r * (D / 32), 0, 0);
+    else if constexpr (kind == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rc_rs, dst, 16, (int)goff, r * 16, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(qb_rs, dst, 16, (int)goff, r * (D * 2), 0, 0);
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
+  using K4 = std::integral_constant<int, 4>;
+  // group A of the tile whose first row is r into A buffer a; group B into B buffer bq
+  auto issue_a = [&](int r, int a) __attribute__((always_inline)) {
+    const int base = L::A0 + a * L::A_BYTES;
+    issue_kind(K0{}, wave, goff_a[0], r, base);
+    issue_kind(K0{}, wave + 8, goff_a[1], r, base);
+    const int j = min(wave + 16, NA - 1);
+    if (j < 20) issue_kind(K1{}, j, goff_a[2], r, base);
+    else if (j == 20) issue_kind(K2{}, j, goff_a[2], r, base);
+    else issue_kind(K3{}, j, goff_a[2], r, base);
+  };
+  auto issue_b = [&](int r, int bq) __attribute__((always_inline)) {
+    const int base = L::B0 + bq * L::B_BYTES;
+    issue_kind(K4{}, wave, goff_b[0], r, base);
+    issue_kind(K4{}, wave + 8, goff_b[1], r, base);
+  };
+  static_assert(JA == 3 && JB == 2, "job slots");
+
+  // ---- query tiles: the query heads of the group, and per head the tiles that see any key ----
+  // (wave-uniform 32-bit scalars: group * D * N * 2 < 2^31 is checked at the boundary)
+  const int j_first = CAUSAL ? (int)(k0 / 64) : 0;
+  const int nj = (int)(N / 64) - j_first;
+  const int ntile = (int)group * nj;
+  auto row_of = [&](int h_, int j_) __attribute__((always_inline)) {   // first row of [head][N]
+    return __builtin_amdgcn_readfirstlane(h_ * (int)N + (j_first + j_) * 64);
+  };
+  auto next = [&](int& h_, int& j_) __attribute__((always_inline)) {
+    if (++j_ == nj) { j_ = 0; ++h_; }
+  };
+  // Step m (0 .. ntile) issues group A of tile m + 1 and group B of tile m; the elementwise waves
+  // take tile m, the product waves tile m - 1.  Buffers rotate: A over three (tile n in n % 3), B
+  // and the scratch over two (n % 2).
+  int hA = 0, jA = 0;                              // tile m + 1
+  next(hA, jA);
+  int hB = 0, jB = 0;                              // tile m
+  int am = 0;                                      // m % 3
+  auto step_loads = [&](int m) __attribute__((always_inline)) {
+    if (m + 1 < ntile) issue_a(row_of(hA, jA), am == 2 ? 0 : am + 1);
+    if (m < ntile) issue_b(row_of(hB, jB), m & 1);
+  };
+  auto step_end = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    hB = hA;
+    jB = jA;
+    next(hA, jA);
+    am = am == 2 ? 0 : am + 1;
+  };
+  issue_a(row_of(0, 0), 0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  if (wave < 4) {
+    // ================= elementwise waves =================
+    const int qh = r4 & 1;
+    const int ql = 32 * qh + l32;                  // this lane's query within the tile
+    // constant operands: K^ (FP4) and V^ (bf16) rows of the wave's two 32-key blocks, in the row
+    // order that makes lane l hold keys kp + 16 (l / 32) + r in S^T / dP^T register r
+    v4i ka[2][2], va[2][8];
+    int ksc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int64_t krow = k0 + 64 * kh + 32 * kt + row_key(l32);
+      const uint8_t* kr = p.k_codes + (bg * N + krow) * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) ka[kt][ks] = *reinterpret_cast<const v4i*>(kr + 16 * hi + 32 * ks);
+      const uint8_t* ksr = p.k_scales + (bg * N + krow) * (D / 32);
+      ksc[kt] = (int)(ksr[hi] | (ksr[2 + hi] << 16));
+      const uint16_t* vr = p.vb + (bg * N + krow) * D;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) va[kt][s] = *reinterpret_cast<const v4i*>(vr + 16 * s + 8 * hi);
+    }
+    // per-lane LDS offsets within a group-A buffer and within a scratch buffer
+    const uint32_t o_qc0 = L::QC + ql * 64 + 16 * (hi ^ swz_code(ql, 4));
+    const uint32_t o_qc1 = L::QC + ql * 64 + 16 * ((hi + 2) ^ swz_code(ql, 4));
+    const uint32_t o_qs = L::QS + 4 * ql, o_rc = L::ROWS + 16 * ql;
+    uint32_t o_do[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o_do[s] = L::DOS + x16_off(ql, 2 * s + hi);
+    // scratch: row ql, keys 64 kh + 32 kt + 16 hi + [0, 16) = chunks 8 kh + 4 kt + 2 hi + {0, 1}
+    uint32_t o_sc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) o_sc[kt][u] = x16_off(ql, 8 * kh + 4 * kt + 2 * hi + u);
+
+    for (int m = 0; m <= ntile; ++m) {
+      step_loads(m);
+      if (m < ntile) {
+        const uint32_t ab = lds0 + L::A0 + am * L::A_BYTES;
+        const uint32_t sb = lds0 + L::S0 + (m & 1) * L::S_BYTES;
+        v4i q0v, q1v, rcv, dov[8];
+        uint32_t qsw;
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %13\n\t"
+            "ds_read_b32 %2, %14\n\t"
+            "ds_read_b128 %3, %15\n\t"
+            "ds_read_b128 %4, %16\n\t"
+            "ds_read_b128 %5, %17\n\t"
+            "ds_read_b128 %6, %18\n\t"
+            "ds_read_b128 %7, %19\n\t"
+            "ds_read_b128 %8, %20\n\t"
+            "ds_read_b128 %9, %21\n\t"
+            "ds_read_b128 %10, %22\n\t"
+            "ds_read_b128 %11, %23\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(q0v), "=&v"(q1v), "=&v"(qsw), "=&v"(rcv), "=&v"(dov[0]), "=&v"(dov[1]), "=&v"(dov[2]),
+              "=&v"(dov[3]), "=&v"(dov[4]), "=&v"(dov[5]), "=&v"(dov[6]), "=&v"(dov[7])
+            : "v"(ab + o_qc0), "v"(ab + o_qc1), "v"(ab + o_qs), "v"(ab + o_rc), "v"(ab + o_do[0]), "v"(ab + o_do[1]),
+              "v"(ab + o_do[2]), "v"(ab + o_do[3]), "v"(ab + o_do[4]), "v"(ab + o_do[5]), "v"(ab + o_do[6]),
+              "v"(ab + o_do[7]));
+        const int qsc = (int)(qsw >> (8 * hi));
+        const float mq = __int_as_float(rcv[0]), ddl = __int_as_float(rcv[3]);
+        const int qrow = (j_first + jB) * 64 + ql;  // query position (causal mask)
+        v4i outp[2][2], outs[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          v16f st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[kt][0]), widen(q0v), v16f{}, 4, 4, 0,
+                                                                   ksc[kt], 0, qsc);
+          st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[kt][1]), widen(q1v), st, 4, 4, 2, ksc[kt], 2,
+                                                               qsc);
+          v16f dp = v16f{};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) dp = mfma_bf16(va[kt][s], dov[s], dp);
+          // register r holds key kp + 16 hi + r
+          if (CAUSAL) {
+            const int jrel = qrow - (int)(k0 + 64 * kh + 32 * kt) - 16 * hi;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (r > jrel) st[r] = -__builtin_inff();
+          }
+          float mx = st[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          const float bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          const int sbyte = p_scale_byte(__builtin_fmaf(bmax, c, -mq), mq);
+          const float sc = __uint_as_float((uint32_t)sbyte << 23);
+          float pr[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -mq));
+          uint32_t aw[8], sw8[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t u = 0;
+            u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q], pr[4 * q + 1], sc, 0);
+            u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
+            aw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 0));
+            aw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 1));
+            sw8[2 * q] = pk_bf16(pr[4 * q] * (dp[4 * q] - ddl), pr[4 * q + 1] * (dp[4 * q + 1] - ddl));
+            sw8[2 * q + 1] = pk_bf16(pr[4 * q + 2] * (dp[4 * q + 2] - ddl), pr[4 * q + 3] * (dp[4 * q + 3] - ddl));
+          }
+          outp[kt][0] = v4i{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3]};
+          outp[kt][1] = v4i{(int)aw[4], (int)aw[5], (int)aw[6], (int)aw[7]};
+          outs[kt][0] = v4i{(int)sw8[0], (int)sw8[1], (int)sw8[2], (int)sw8[3]};
+          outs[kt][1] = v4i{(int)sw8[4], (int)sw8[5], (int)sw8[6], (int)sw8[7]};
+        }
+        // P~ at +0, dS at +16384 of the scratch buffer (the trailing nop covers the store-data
+        // hazard of the last 128-bit store)
+        asm volatile(
+            "ds_write_b128 %0, %4\n\t"
+            "ds_write_b128 %1, %5\n\t"
+            "ds_write_b128 %2, %6\n\t"
+            "ds_write_b128 %3, %7\n\t"
+            "ds_write_b128 %0, %8 offset:16384\n\t"
+            "ds_write_b128 %1, %9 offset:16384\n\t"
+            "ds_write_b128 %2, %10 offset:16384\n\t"
+            "ds_write_b128 %3, %11 offset:16384\n\t"
+            "s_nop 1"
+            :
+            : "v"(sb + o_sc[0][0]), "v"(sb + o_sc[0][1]), "v"(sb + o_sc[1][0]), "v"(sb + o_sc[1][1]),
+              "v"(outp[0][0]), "v"(outp[0][1]), "v"(outp[1][0]), "v"(outp[1][1]), "v"(outs[0][0]), "v"(outs[0][1]),
+              "v"(outs[1][0]), "v"(outs[1][1])
+            : "memory");
+      }
+      step_end();
+    }
+  } else {
+    // ================= product waves =================
+    const int chh = r4 & 1;                        // 64-channel half
+    v16f dv[2][2], dk[2][2];                       // [key block kt][channel tile ct]
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        dv[kt][ct] = v16f{};
+        dk[kt][ct] = v16f{};
+      }
+    // transposing loads.  In each 16-lane group, lane i supplies four consecutive elements of row
+    // base + i / 4 and lane j receives element j of rows base .. base + 3.
+    //  * scratch (B operands): keys 64 kh + 32 kt + 16 gh + 4 (gi % 4) of rows 16 s + 8 hi + gi / 4
+    //    and + 4: lane l receives key 64 kh + 32 kt + l % 32 of queries 16 s + 8 hi + [0, 8);
+    //  * dO / l and Q^ (A operands): channels 64 chh + 32 ct + 16 gh + 4 (gi % 4) of the same rows:
+    //    lane l receives channel 64 chh + 32 ct + l % 32 of those queries.
+    // The swizzle is periodic in 16 rows, so step s (rows + 16 s) is an immediate offset of 4096 s.
+    const int qa = 8 * hi + (gi >> 2);
+    uint32_t o_p[2][2], o_a[2][2];                 // [kt or ct][u: rows qa or qa + 4]
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = 64 * kh + 32 * t + 16 * gh + 4 * (gi & 3);
+        o_p[t][u] = x16_off(qa + 4 * u, key >> 3) + 2 * (key & 7);
+        const int ch = 64 * chh + 32 * t + 16 * gh + 4 * (gi & 3);
+        o_a[t][u] = x16_off(qa + 4 * u, ch >> 3) + 2 * (ch & 7);
+      }
+    for (int m = 0; m <= ntile; ++m) {
+      step_loads(m);
+      if (m >= 1) {
+        const int n = m - 1;                       // the tile of these products (A buffer n % 3)
+        const uint32_t ab = lds0 + L::A0 + (am == 0 ? 2 : am - 1) * L::A_BYTES + L::DOS;
+        const uint32_t bb = lds0 + L::B0 + (n & 1) * L::B_BYTES;
+        const uint32_t sb = lds0 + L::S0 + (n & 1) * L::S_BYTES;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v2i rp[2][2], rs[2][2], ro[2][2], rq[2][2];
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %16 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %1, %17 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %2, %18 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %3, %19 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %4, %16 offset:%c29\n\t"
+              "ds_read_b64_tr_b16 %5, %17 offset:%c29\n\t"
+              "ds_read_b64_tr_b16 %6, %18 offset:%c29\n\t"
+              "ds_read_b64_tr_b16 %7, %19 offset:%c29\n\t"
+              "ds_read_b64_tr_b16 %8, %20 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %9, %21 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %10, %22 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %11, %23 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %12, %24 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %13, %25 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %14, %26 offset:%c28\n\t"
+              "ds_read_b64_tr_b16 %15, %27 offset:%c28\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(rp[0][0]), "=&v"(rp[0][1]), "=&v"(rp[1][0]), "=&v"(rp[1][1]), "=&v"(rs[0][0]), "=&v"(rs[0][1]),
+                "=&v"(rs[1][0]), "=&v"(rs[1][1]), "=&v"(ro[0][0]), "=&v"(ro[0][1]), "=&v"(ro[1][0]), "=&v"(ro[1][1]),
+                "=&v"(rq[0][0]), "=&v"(rq[0][1]), "=&v"(rq[1][0]), "=&v"(rq[1][1])
+              : "v"(sb + o_p[0][0]), "v"(sb + o_p[0][1]), "v"(sb + o_p[1][0]), "v"(sb + o_p[1][1]),
+                "v"(ab + o_a[0][0]), "v"(ab + o_a[0][1]), "v"(ab + o_a[1][0]), "v"(ab + o_a[1][1]),
+                "v"(bb + o_a[0][0]), "v"(bb + o_a[0][1]), "v"(bb + o_a[1][0]), "v"(bb + o_a[1][1]),
+                "n"(4096 * s), "n"(4096 * s + 16384));
+          v4i bp[2], bs[2], ao[2], aq[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            bp[t] = v4i{rp[t][0][0], rp[t][0][1], rp[t][1][0], rp[t][1][1]};
+            bs[t] = v4i{rs[t][0][0], rs[t][0][1], rs[t][1][0], rs[t][1][1]};
+            ao[t] = v4i{ro[t][0][0], ro[t][0][1], ro[t][1][0], ro[t][1][1]};
+            aq[t] = v4i{rq[t][0][0], rq[t][0][1], rq[t][1][0], rq[t][1][1]};
+          }
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              dv[kt][ct] = mfma_bf16(ao[ct], bp[kt], dv[kt][ct]);
+              dk[kt][ct] = mfma_bf16(aq[ct], bs[kt], dk[kt][ct]);
+            }
+        }
+      }
+      step_end();
+    }
+    // ---- store: lane holds key k0 + 64 kh + 32 kt + l32, channels 64 chh + 32 ct + 8 a + 4 hi + [0, 4) ----
+    const float sc = p.scale_nat;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int64_t key = k0 + 64 * kh + 32 * kt + l32;
+      uint16_t* dvr = p.dv + (bg * N + key) * D;
+      uint16_t* dkr = p.dk + (bg * N + key) * D;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int ch = 64 * chh + 32 * ct + 8 * a4 + 4 * hi;
+          *reinterpret_cast<uint2*>(dvr + ch) = make_uint2(pk_bf16(dv[kt][ct][4 * a4], dv[kt][ct][4 * a4 + 1]),
+                                                           pk_bf16(dv[kt][ct][4 * a4 + 2], dv[kt][ct][4 * a4 + 3]));
+          *reinterpret_cast<uint2*>(dkr + ch) =
+              make_uint2(pk_bf16(sc * dk[kt][ct][4 * a4], sc * dk[kt][ct][4 * a4 + 1]),
+                         pk_bf16(sc * dk[kt][ct][4 * a4 + 2], sc * dk[kt][ct][4 * a4 + 3]));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // 4. dQ.  Workgroup = W waves of 32 query rows; key tiles of 64 staged in LDS.
 template <int D>
 struct DqLds {
@@ -598,7 +1027,7 @@ bwd_dq_kernel(BwdParams p) {
   // lane's global byte offset (within tile 0) and LDS destination of job j
   auto job_goff_of = [&](int j) -> uint32_t {
     if (j < NKC) {
-      const int cidx = 64 * j + lane, s = cidx / KCH, cc = (cidx % KCH) ^ swz_small(s, KCH);
+      const int cidx = 64 * j + lane, s = cidx / KCH, cc = (cidx % KCH) ^ swz_code(s, KCH);
       return (32 * (s >> 5) + row_key(s & 31)) * (D / 2) + 16 * cc;
     } else if (j < NKC + NVB) {
       const int cidx = 64 * (j - NKC) + lane, s = cidx / VC, cc = (cidx % VC) ^ swz_big(s, VC);
@@ -682,7 +1111,7 @@ bwd_dq_kernel(BwdParams p) {
       v16f st = v16f{};
 #pragma unroll
       for (int ks = 0; ks < KS_STEPS; ++ks) {
-        const int pc = (hi + 2 * ks) ^ swz_small(slot, KCH);
+        const int pc = (hi + 2 * ks) ^ swz_code(slot, KCH);
         const v4i ka = *reinterpret_cast<const v4i*>(base + L::KC + slot * (D / 2) + 16 * pc);
         if (ks == 0)
           st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka), widen(qb[0]), st, 4, 4, 0, ksc, 0, qsc);
@@ -762,7 +1191,10 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
-  if (p.N % 128 == 0)
+  if (D == 128 && p.N % 128 == 0)
+    hipLaunchKernelGGL((bwd_dkdv_ws_kernel<CAUSAL>), dim3((unsigned)((p.N / 128) * p.Hkv * p.B)), dim3(512), 0,
+                       stream, p);
+  else if (p.N % 128 == 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8, CAUSAL>), dim3((unsigned)((p.N / 128) * p.Hkv * p.B)), dim3(512), 0,
                        stream, p);
   else
@@ -796,25 +1228,33 @@ BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
   return w;
 }
 
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p0, hipStream_t stream) {
+  // d = 128 with N % 128 = 0 runs the producer/consumer dK/dV kernel, which reads row-major
+  // Q^ (bf16) and dO / l written by the row pass into the regions of the transposed copies
+  const bool ws = p0.d == 128 && p0.N % 128 == 0;
+  BwdParams p = p0;
+  p.qb = ws ? p.qt : nullptr;
+  p.dos = ws ? p.dot : nullptr;
   const int64_t rows = p.B * p.Hq * p.N;
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p.o, p.dout, p.m,
-                     p.l, p.rowc, rows, (int)p.d);
+                     p.l, p.rowc, rows, (int)p.d, p.q_codes, p.q_scales, p.qb, p.dos);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t d = p.d, N = p.N;
   // V^ codes (block-major [N/32][d][16]) -> V^ bf16 [N][d]
   hipLaunchKernelGGL((bwd_transpose_kernel<true, true>), dim3((unsigned)(N / 64), (unsigned)(d / 64), (unsigned)(p.B * p.Hkv)),
                      dim3(256), 0, stream, p.v_codes, p.v_scales, p.vb, d, N);
-  // K^ codes [N][d/2] -> K^T bf16 [d][N]; Q^ likewise; dO bf16 [N][d] -> dO^T [d][N]
+  // K^ codes [N][d/2] -> K^T bf16 [d][N] (dQ); for the other dK/dV kernel also Q^ likewise and
+  // dO bf16 [N][d] -> dO^T [d][N], carrying each query's 1/l: dV^T = dO^T diag(1/l) P~
   hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hkv)),
                      dim3(256), 0, stream, p.k_codes, p.k_scales, p.kt, N, d);
-  hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
-                     dim3(256), 0, stream, p.q_codes, p.q_scales, p.qt, N, d);
-  // dO^T carries each query's 1/l: dV^T = dO^T diag(1/l) P~ with P~ exact in bf16
-  hipLaunchKernelGGL(bwd_transpose_kernel<false>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
-                     dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d,
-                     (const float*)p.rowc + 1);
+  if (!ws) {
+    hipLaunchKernelGGL(bwd_transpose_kernel<true>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
+                       dim3(256), 0, stream, p.q_codes, p.q_scales, p.qt, N, d);
+    hipLaunchKernelGGL(bwd_transpose_kernel<false>, dim3((unsigned)(d / 64), (unsigned)(N / 64), (unsigned)(p.B * p.Hq)),
+                       dim3(256), 0, stream, (const uint8_t*)p.dout, (const uint8_t*)nullptr, p.dot, N, d,
+                       (const float*)p.rowc + 1);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.d == 128) return p.causal ? launch_main<128, true>(p, stream) : launch_main<128, false>(p, stream);

@@ -56,11 +56,14 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   // workspace (carved by the host layer, see BwdWorkspace)
-  float* rowc;      // per query row (m * log2(e), 1 / l, D = rowsum(dO * O), 0), [B, Hq, N, 4]
+  float* rowc;      // per query row (m * log2(e), 1 / l, D = rowsum(dO * O), D / l), [B, Hq, N, 4]
   uint16_t* vb;     // V^ dequantized, bf16 [B, Hkv, N, d]
   uint16_t* kt;     // K^ dequantized and transposed, bf16 [B, Hkv, d, N]
   uint16_t* qt;     // Q^ dequantized and transposed, bf16 [B, Hq, d, N]
   uint16_t* dot;    // dO transposed, each query row times its 1/l, bf16 [B, Hq, d, N]
+  // the d = 128 dK/dV path reads row-major copies instead (same workspace regions as qt, dot):
+  uint16_t* qb;     // Q^ dequantized, bf16 [B, Hq, N, d]
+  uint16_t* dos;    // dO times each row's 1/l, bf16 [B, Hq, N, d]
   int64_t B, Hq, Hkv, N, d;
   int causal;
   float c;          // softmax_scale * log2(e)

@@ -40,7 +40,8 @@ def run_gpu(q, k, v, do, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N,d,Hq,Hkv", [(64, 128, 1, 1), (192, 128, 4, 2), (256, 64, 2, 2), (128, 128, 2, 1)])
+@pytest.mark.parametrize("N,d,Hq,Hkv", [(64, 128, 1, 1), (192, 128, 4, 2), (256, 64, 2, 2), (128, 128, 2, 1),
+                                        (256, 128, 4, 2), (384, 128, 2, 2)])
 def test_small_shapes_full(N, d, Hq, Hkv, causal):
     rng = np.random.default_rng(100 + N + d + Hq + int(causal))
     q = W.round_to_bf16(rng.standard_normal((1, Hq, N, d)) * 1.5)

@@ -40,16 +40,6 @@ __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
 }
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
-// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
-
 // XOR swizzle of the 16-byte chunks of an FP4 code row in LDS (64 B = 4 chunks at d = 128, 32 B =
 // 2 chunks at d = 64), so that 16 lanes reading one logical chunk of 16 consecutive rows hit 16
 // distinct 4-bank groups.

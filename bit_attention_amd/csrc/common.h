@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attnfp4 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -35,6 +38,16 @@ __device__ __forceinline__ int swz_big(int row, int nchunks) {
 // Raw buffer resource over [base, base + bytes) (gfx9 dword 3; out-of-range loads return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).

@@ -98,3 +98,24 @@ def test_qat_workload_full_size_sampled():
                          key_blocks=blocks)
     print("qat cosine vs exact-attention gradients: dQ %.4f dK %.4f dV %.4f" % (
         cosine(dq[0, 0, rows], ex[0][0, 0]), cosine(dk[0, 0, keys], ex[1][0, 0]), cosine(dv[0, 0, keys], ex[2][0, 0])))
+
+
+def test_causal_gqa_mid_size_sampled():
+    """Causal GQA backward at a size with many query tiles per key block and key blocks past the
+    first (the causal start tile, the walk over both query heads of a KV head): sampled query rows
+    (dQ) and sampled 32-key blocks (dK, dV, summed over the group) against the oracle."""
+    rng = np.random.default_rng(2048)
+    B, Hq, Hkv, N, d = 1, 4, 2, 2048, 128
+    q = W.round_to_bf16(rng.standard_normal((B, Hq, N, d)) * 1.2)
+    k = W.round_to_bf16(rng.standard_normal((B, Hkv, N, d)))
+    v = W.round_to_bf16(rng.standard_normal((B, Hkv, N, d)))
+    do = W.round_to_bf16(rng.standard_normal((B, Hq, N, d)) * 0.1)
+    o, m, l, dq, dk, dv = run_gpu(q, k, v, do, True)
+    rows = W.sample_rows(N, 160)
+    blocks = np.array([0, 3, 4, 5, 31, 32, 33, 47, 60, N // 32 - 1])
+    keys = (blocks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    m_ref = oracle.attn_row_max(q, k, causal=True)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, o, do, m_ref, l, causal=True, rows=rows, key_blocks=blocks)
+    for name, g, r in (("dQ", dq[:, :, rows], rq), ("dK", dk[:, :, keys], rk), ("dV", dv[:, :, keys], rv)):
+        info = compare(g, r, "causal gqa N2048 " + name)
+        print("causal gqa N2048 %s rel-L2 %.3e max-abs %.3e" % (name, info["rel_l2"], info["max_abs"]))

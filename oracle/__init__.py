@@ -23,6 +23,9 @@ that each step can be checked by eye against the pages it follows:
   4-bit GEMMs inside FlashAttention with the online-softmax state kept in a
   wider format.
 
+* TetraJet-v2, RFQ and HiFA4 abstracts -- NVFP4 and HIF4 named as other
+  4-bit formats; nv.py holds an NVFP4-style reading of that name.
+
 Parity status of each function is stated in its module header.
 """
 
@@ -38,6 +41,18 @@ from .mx import (  # noqa: F401
     fake_quant_mx,
     pack_nibbles,
     unpack_nibbles,
+)
+from .nv import (  # noqa: F401
+    E4M3_POS,
+    NV_BLOCK,
+    NV_TENSOR_DIV,
+    decode_e4m3,
+    e4m3_round_codes,
+    nv_tensor_scale,
+    quantize_nv,
+    dequantize_nv,
+    fake_quant_nv,
+    nv_p_fake_quant,
 )
 from .attention import (  # noqa: F401
     BC,

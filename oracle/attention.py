@@ -58,13 +58,17 @@ D = rowsum(P o dP) with quantizers off.  Cache forward
 (tests/test_oracle_kvcache.py): quantizers off -> textbook attention over
 the visible keys; quantizers on -> rows of the full forward at those
 positions; Q = 0 -> mean of V^ over the visible keys (ragged lengths); empty
-rows; cache contents past the length have no effect.
+rows; cache contents past the length have no effect.  NVFP4-style forward
+(fmt="nv", tests/test_oracle_nv.py): quantizers off -> textbook attention;
+Q = 0 and identical keys -> mean of V^ (causal: prefix mean), l = count;
+V -> 2^k V scales O exactly; sampled rows match the full result.
 """
 
 import numpy as np
 
 from .efq import efq_fake_quant
 from .mx import fake_quant_mx
+from .nv import fake_quant_nv, nv_p_fake_quant, nv_tensor_scale
 
 BC = 64  # key-tile width; part of the definition of P quantization
 
@@ -137,7 +141,7 @@ def _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant):
     return O, m, l
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp"):
+def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp", fmt="mx"):
     """Tile-by-tile fake-quantized attention forward.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (values read exactly as float64).
@@ -145,16 +149,29 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_
     quant=False replaces all four quantizers by the identity.
     p_rule: "exp" -- P~ = MXFP4(exp(s - m)) (exp-then-quantize, the definition); "efq" -- P~ from
     the EFQ-Softmax codes of the shifted scores (oracle/efq.py, a reading of the pages).
+    fmt: "mx" -- MXFP4 operands; "nv" -- the NVFP4-style reading of oracle/nv.py (16-element
+    blocks, E4M3 block scales, one fp32 scale per tensor of Q, K and V; P~ per 16 keys), with
+    the exp rule only.
     Returns (O [B, Hq, R, d], m [B, Hq, R], l [B, Hq, R]), float64.
     """
     if p_rule not in ("exp", "efq"):
         raise ValueError("p_rule must be 'exp' or 'efq'")
+    if fmt not in ("mx", "nv") or (fmt == "nv" and p_rule != "exp"):
+        raise ValueError("fmt must be 'mx', or 'nv' with p_rule 'exp'")
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     B, Hq, Hkv, N, d = _check_shapes(q, k, v)
     if N % bc:
         raise ValueError("N must be a multiple of the tile width")
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     fq = fake_quant_mx if quant else _identity
+    fq_q = fq_k = fq_v = fq_p = fq
+    if fmt == "nv" and quant:
+        # one tensor scale per operand, taken over the whole tensor (also when sampling rows)
+        gq, gk, gv = (nv_tensor_scale(t)[0] for t in (q, k, v))
+        fq_q = lambda x, axis: fake_quant_nv(x, axis, gq)   # noqa: E731
+        fq_k = lambda x, axis: fake_quant_nv(x, axis, gk)   # noqa: E731
+        fq_v = lambda x, axis: fake_quant_nv(x, axis, gv)   # noqa: E731
+        fq_p = nv_p_fake_quant
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.shape[0]
     group = Hq // Hkv
@@ -165,11 +182,12 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_
     limit = rows.copy() if causal else np.full(R, N - 1, dtype=np.int64)
     for b in range(B):
         for g in range(Hkv):
-            k_hat = fq(k[b, g], axis=-1)          # along the head dim
-            v_hat = fq(v[b, g], axis=0)           # along the sequence
+            k_hat = fq_k(k[b, g], axis=-1)        # along the head dim
+            v_hat = fq_v(v[b, g], axis=0)         # along the sequence
             for h in range(g * group, (g + 1) * group):
-                q_hat = fq(q[b, h][rows], axis=-1)
-                O[b, h], M[b, h], L[b, h] = _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant)
+                q_hat = fq_q(q[b, h][rows], axis=-1)
+                O[b, h], M[b, h], L[b, h] = _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq_p, p_rule,
+                                                      quant)
     return O, M, L
 
 

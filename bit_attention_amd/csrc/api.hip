@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -236,6 +236,66 @@ int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* a, void* stream) {
   p.scale_nat = (float)s;
   hipError_t e = attnfp4::launch_bwd(p, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return ATTN_FP4_E_UNSUPPORTED;
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int32_t attn_fp4_nv_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32_t axis, void* codes,
+                             void* scales, float* tensor_scale, void* stream) {
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return ATTN_FP4_E_INVALID_ARG;
+  if (tensor_scale == nullptr || (reinterpret_cast<uintptr_t>(tensor_scale) & 7u) != 0) return ATTN_FP4_E_INVALID_ARG;
+  if (bh <= 0 || n <= 0 || d <= 0 || d % 32 != 0) return ATTN_FP4_E_INVALID_ARG;
+  if (axis != 0 && axis != 1) return ATTN_FP4_E_INVALID_ARG;
+  if (axis == 1 && (n % 16 != 0 || bh > 65535 || d / 32 > 65535 || (n + 127) / 128 > 0x7FFFFFFF))
+    return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  hipError_t e = attnfp4::launch_nv_quantize(x, bh, n, d, axis, codes, scales, tensor_scale, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int64_t attn_fp4_nv_fwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {
+  if (check_dims(B, Hq, Hkv, N, d) != ATTN_FP4_OK) return -1;
+  return attnfp4::nv_fwd_workspace_layout(B, Hq, Hkv, N, d).total;
+}
+
+int32_t attn_fp4_nv_fwd(const attn_fp4_nv_fwd_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_dims(a->B, a->Hq, a->Hkv, a->N, a->d);
+  if (st != ATTN_FP4_OK) return st;
+  const void* ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes,
+                        a->v_scales, a->o, a->m, a->l};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_FP4_E_INVALID_ARG;
+  const float* ts[] = {a->q_tensor_scale, a->k_tensor_scale, a->v_tensor_scale};
+  for (const float* t : ts)
+    if (t == nullptr || (reinterpret_cast<uintptr_t>(t) & 7u) != 0) return ATTN_FP4_E_INVALID_ARG;
+  if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
+  const attnfp4::NvWorkspace ws = attnfp4::nv_fwd_workspace_layout(a->B, a->Hq, a->Hkv, a->N, a->d);
+  if (a->workspace == nullptr || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 ||
+      a->workspace_bytes < ws.total)
+    return ATTN_FP4_E_WORKSPACE;
+  // the kernel addresses one KV head's bf16 [N, d] operands with 32-bit buffer offsets
+  if (a->N * a->d * 2 > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_UNSUPPORTED;
+  st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  uint8_t* w = (uint8_t*)a->workspace;
+  attnfp4::NvFwdParams p;
+  p.qb = (const uint16_t*)(w + ws.qb);
+  p.kb = (const uint16_t*)(w + ws.kb);
+  p.vt = (const uint16_t*)(w + ws.vt);
+  p.q_ts = a->q_tensor_scale;
+  p.k_ts = a->k_tensor_scale;
+  p.v_ts = a->v_tensor_scale;
+  p.o = (uint16_t*)a->o;
+  p.m = a->m;
+  p.l = a->l;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.N = a->N;
+  p.scale_nat = resolve_scale(a->softmax_scale, a->d);
+  hipError_t e = attnfp4::launch_nv_fwd(p, a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes, a->v_scales,
+                                        (int)a->d, a->causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
 }
 

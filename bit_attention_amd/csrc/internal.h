@@ -76,6 +76,33 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
 
+// NVFP4-style forward: the operands dequantized to bf16 (E2M1 * E4M3 scale, exact) in the
+// workspace, and the device-resident fp32 tensor scales.
+struct NvFwdParams {
+  const uint16_t* qb;   // Q^ / G_Q, bf16 [B, Hq, N, d]
+  const uint16_t* kb;   // K^ / G_K, bf16 [B, Hkv, N, d]
+  const uint16_t* vt;   // V^ / G_V transposed, bf16 [B, Hkv, d, N]
+  const float* q_ts;    // tensor scales G (first float of each attn_fp4_nv_quantize output)
+  const float* k_ts;
+  const float* v_ts;
+  uint16_t* o;
+  float* m;
+  float* l;
+  int64_t B, Hq, Hkv, N;
+  float scale_nat;      // softmax_scale
+};
+
+struct NvWorkspace {
+  int64_t qb, kb, vt, total;
+};
+NvWorkspace nv_fwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
+
+hipError_t launch_nv_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes, void* scales,
+                              float* ts, hipStream_t stream);
+hipError_t launch_nv_fwd(const NvFwdParams& p, const void* q_codes, const void* q_scales, const void* k_codes,
+                         const void* k_scales, const void* v_codes, const void* v_scales, int d, bool causal,
+                         hipStream_t stream);
+
 hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int axis, void* codes,
                            void* scales, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);

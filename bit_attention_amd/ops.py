@@ -33,6 +33,9 @@ EXPORTED = (
     "attn_fp4_fwd_kvcache_workspace_bytes",
     "attn_fp4_bwd_workspace_bytes",
     "attn_fp4_bwd_recompute",
+    "attn_fp4_nv_quantize",
+    "attn_fp4_nv_fwd_workspace_bytes",
+    "attn_fp4_nv_fwd",
 )
 
 
@@ -52,6 +55,21 @@ class FwdArgs(ctypes.Structure):
         ("N", ctypes.c_int64), ("d", ctypes.c_int64),
         ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("p_rule", ctypes.c_int32),
+    ]
+
+
+class NvFwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_codes", ctypes.c_void_p), ("q_scales", ctypes.c_void_p),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("q_tensor_scale", ctypes.c_void_p), ("k_tensor_scale", ctypes.c_void_p),
+        ("v_tensor_scale", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("N", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
     ]
 
 
@@ -114,6 +132,14 @@ def lib():
         L.attn_fp4_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 5
         L.attn_fp4_bwd_recompute.restype = ctypes.c_int32
         L.attn_fp4_bwd_recompute.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+        L.attn_fp4_nv_quantize.restype = ctypes.c_int32
+        L.attn_fp4_nv_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        L.attn_fp4_nv_fwd_workspace_bytes.restype = ctypes.c_int64
+        L.attn_fp4_nv_fwd_workspace_bytes.argtypes = [ctypes.c_int64] * 5
+        L.attn_fp4_nv_fwd.restype = ctypes.c_int32
+        L.attn_fp4_nv_fwd.argtypes = [ctypes.POINTER(NvFwdArgs), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -293,3 +319,72 @@ def attn_fp4_bwd_recompute(q_codes, q_scales, k_codes, k_scales, v_codes, v_scal
                 workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale))
     _check(lib().attn_fp4_bwd_recompute(ctypes.byref(a), _stream(stream)), "attn_fp4_bwd_recompute")
     return dq, dk, dv
+
+
+def attn_fp4_nv_quantize(x, axis, codes=None, scales=None, tensor_scale=None, stream=None):
+    """NVFP4-style quantization of bf16 ``x`` [..., n, d] (16-element blocks, E4M3 scales).
+
+    axis=0: along d -> codes [..., n, d/2], scales [..., n, d/16].
+    axis=1: along n, transposed -> codes [..., d, n/2], scales [..., d, n/16].
+    tensor_scale: float32 [2] on the device, written with (G, amax).
+    Returns (codes, scales, tensor_scale).
+    """
+    _dev(x, torch.bfloat16, "x")
+    *lead, n, d = x.shape
+    bh = int(math.prod(lead)) if lead else 1
+    if axis == 0:
+        cshape, sshape = (*lead, n, d // 2), (*lead, n, d // 16)
+    else:
+        cshape, sshape = (*lead, d, n // 2), (*lead, d, n // 16)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    if tensor_scale is None:
+        tensor_scale = torch.empty(2, dtype=torch.float32, device=x.device)
+    _check(lib().attn_fp4_nv_quantize(_ptr(x), bh, n, d, int(axis), _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+                                      _stream(stream)), "attn_fp4_nv_quantize")
+    return codes, scales, tensor_scale
+
+
+def attn_fp4_nv_fwd_workspace_bytes(B, Hq, Hkv, N, d):
+    return int(lib().attn_fp4_nv_fwd_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def attn_fp4_nv_fwd(q_codes, q_scales, q_ts, k_codes, k_scales, k_ts, v_codes, v_scales, v_ts, causal=False,
+                    softmax_scale=0.0, o=None, m=None, l=None, workspace=None, stream=None):
+    """Attention forward on NVFP4-style operands (layouts and tensor scales of attn_fp4_nv_quantize).
+
+    q_codes [B, Hq, N, d/2]; k_codes [B, Hkv, N, d/2]; v_codes [B, Hkv, d, N/2]; *_ts float32 [2].
+    Returns (o bf16 [B, Hq, N, d], m fp32 [B, Hq, N], l fp32 [B, Hq, N]).
+    """
+    B, Hq, N, dh = q_codes.shape
+    d = 2 * dh
+    Hkv = k_codes.shape[1]
+    for t, name in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
+                    (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, torch.uint8, name)
+    for t, name in ((q_ts, "q_ts"), (k_ts, "k_ts"), (v_ts, "v_ts")):
+        _dev(t, torch.float32, name)
+    if k_codes.shape != (B, Hkv, N, dh) or v_codes.shape != (B, Hkv, d, N // 2):
+        raise ValueError("inconsistent operand shapes")
+    if q_scales.shape != (B, Hq, N, d // 16) or k_scales.shape != (B, Hkv, N, d // 16) \
+            or v_scales.shape != (B, Hkv, d, N // 16):
+        raise ValueError("inconsistent scale shapes")
+    dev = q_codes.device
+    if o is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    if m is None:
+        m = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    need = attn_fp4_nv_fwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if need < 0:
+        raise AttnFp4Error(1, "attn_fp4_nv_fwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    a = NvFwdArgs(_ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                  _ptr(q_ts), _ptr(k_ts), _ptr(v_ts), _ptr(o), _ptr(m), _ptr(l), _ptr(workspace), workspace.numel(),
+                  B, Hq, Hkv, N, d, int(bool(causal)), float(softmax_scale))
+    _check(lib().attn_fp4_nv_fwd(ctypes.byref(a), _stream(stream)), "attn_fp4_nv_fwd")
+    return o, m, l

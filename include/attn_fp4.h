@@ -256,6 +256,94 @@ int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t
  */
 int32_t attn_fp4_bwd_recompute(const attn_fp4_bwd_args* args, void* stream);
 
+/*
+ * ---- NVFP4-style operands (a second scale format) ----
+ *
+ * The pages name NVFP4 as a 4-bit format (TetraJet-v2 abstract) and compare
+ * it with MXFP4 and HiF4 (RFQ abstract; HiFA4 abstract) but do not define
+ * it.  This library's reading is the published NVFP4 layout:
+ *  - E2M1 codes as above (two per byte, same nibble order);
+ *  - one unsigned FP8 E4M3 block scale byte per 16 consecutive elements of
+ *    the contraction axis (4 exponent bits, bias 7, 3 mantissa bits,
+ *    subnormals, largest 448 = 0x7E; 0x7F is never written);
+ *  - one fp32 tensor scale G per tensor.
+ * Every step is fp32 with round-to-nearest-even:
+ *   G = max(amax / 2688, 2^-117) over the whole tensor (2688 = 6 * 448);
+ *   per block s = amax_block / (6 G), S = E4M3(s), ties to the even mantissa,
+ *   saturating at 448; code = E2M1(x / (S G)), ties to even, saturating at
+ *   6, sign kept; a block with S = 0 gets sign-only codes.
+ *   value = G * S * E2M1(code).
+ */
+
+/*
+ * attn_fp4_nv_quantize -- bf16 -> NVFP4-style codes, E4M3 block scales and
+ * the tensor scale (three launches on `stream`: clear, tensor amax, encode).
+ *   x       bf16 [bh, n, d], device.
+ *   axis 0  along d (Q, K): codes [bh, n, d/2], scales [bh, n, d/16].
+ *   axis 1  along n (V), transposed: codes [bh, d, n/2] (byte j of channel
+ *           c holds tokens 2j (low nibble) and 2j+1), scales [bh, d, n/16].
+ *           Requires n % 16 == 0.
+ *   tensor_scale  device float[2], 8-byte aligned (output): [0] = G, [1] =
+ *           the tensor's amax.  Pass [0] to attn_fp4_nv_fwd.
+ *   Requires d % 32 == 0, bh, n > 0.  Codes, scales and G are bit-exact with
+ *   the rule above.
+ * Errors: ATTN_FP4_E_INVALID_ARG (null or misaligned pointer, sizes, axis),
+ * ATTN_FP4_E_UNSUPPORTED_DEVICE, ATTN_FP4_E_HIP.
+ */
+int32_t attn_fp4_nv_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32_t axis, void* codes,
+                             void* scales, float* tensor_scale, void* stream);
+
+/*
+ * NVFP4-style forward arguments.  Layouts (device, contiguous):
+ *   q_codes [B, Hq, N, d/2]  q_scales [B, Hq, N, d/16]    (attn_fp4_nv_quantize axis 0)
+ *   k_codes [B, Hkv, N, d/2] k_scales [B, Hkv, N, d/16]   (axis 0)
+ *   v_codes [B, Hkv, d, N/2] v_scales [B, Hkv, d, N/16]   (axis 1)
+ *   *_tensor_scale  device float* to each operand's G (8-byte aligned)
+ *   o, m, l as for attn_fp4_fwd (l is the row sum of the quantized P, in
+ *   probability units).
+ *   workspace: device memory, 256-byte aligned, of at least
+ *   attn_fp4_nv_fwd_workspace_bytes(...) bytes (the operands dequantized to
+ *   bf16); contents on entry do not matter and are clobbered.
+ */
+typedef struct {
+  const void* q_codes;
+  const void* q_scales;
+  const void* k_codes;
+  const void* k_scales;
+  const void* v_codes;
+  const void* v_scales;
+  const float* q_tensor_scale;
+  const float* k_tensor_scale;
+  const float* v_tensor_scale;
+  void* o;
+  float* m;
+  float* l;
+  void* workspace;
+  int64_t workspace_bytes;
+  int64_t B, Hq, Hkv, N, d;
+  int32_t causal;
+  float softmax_scale;
+} attn_fp4_nv_fwd_args;
+
+/* Workspace bytes attn_fp4_nv_fwd needs for these sizes (< 0 on invalid sizes). */
+int64_t attn_fp4_nv_fwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
+
+/*
+ * attn_fp4_nv_fwd -- the attention forward of attn_fp4_fwd (exp-then-quantize,
+ * ascending 64-key tiles, one quantized P for numerator and denominator) over
+ * NVFP4-style operands.  P is requantized per 16 keys in the same format with
+ * the tensor scale of amax = 1: S = E4M3(max p * 448), P~ = E2M1(p * 2688 / S)
+ * * S / 2688.  gfx950's block-scaled matrix core takes power-of-two scales per
+ * 32 elements only, so both products run on the bf16 matrix core, where
+ * E2M1 * E4M3 values are exact; fp32 accumulation and softmax state.
+ * Supported: d == 128 or d == 64, N % 64 == 0, Hq % Hkv == 0.
+ * Errors: ATTN_FP4_E_INVALID_ARG, ATTN_FP4_E_WORKSPACE,
+ * ATTN_FP4_E_UNSUPPORTED (N * d * 2 above 2^31 - 1: one head's bf16 operand
+ * exceeds the kernel's 32-bit buffer offsets), ATTN_FP4_E_UNSUPPORTED_DEVICE,
+ * ATTN_FP4_E_HIP.
+ */
+int32_t attn_fp4_nv_fwd(const attn_fp4_nv_fwd_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,7 +141,8 @@ def _fwd_rows(q_hat, k_hat, v_hat, limit, scale, bc, fq, p_rule, quant):
     return O, m, l
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp", fmt="mx"):
+def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_rule="exp", fmt="mx",
+             nv_tensor_scales=None):
     """Tile-by-tile fake-quantized attention forward.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (values read exactly as float64).
@@ -151,7 +152,8 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_
     the EFQ-Softmax codes of the shifted scores (oracle/efq.py, a reading of the pages).
     fmt: "mx" -- MXFP4 operands; "nv" -- the NVFP4-style reading of oracle/nv.py (16-element
     blocks, E4M3 block scales, one fp32 scale per tensor of Q, K and V; P~ per 16 keys), with
-    the exp rule only.
+    the exp rule only.  nv_tensor_scales: (G_Q, G_K, G_V) of the whole tensors when q, k, v are
+    slices of them (default: the scales of q, k, v themselves).
     Returns (O [B, Hq, R, d], m [B, Hq, R], l [B, Hq, R]), float64.
     """
     if p_rule not in ("exp", "efq"):
@@ -167,7 +169,8 @@ def attn_fwd(q, k, v, causal=False, scale=None, bc=BC, quant=True, rows=None, p_
     fq_q = fq_k = fq_v = fq_p = fq
     if fmt == "nv" and quant:
         # one tensor scale per operand, taken over the whole tensor (also when sampling rows)
-        gq, gk, gv = (nv_tensor_scale(t)[0] for t in (q, k, v))
+        gq, gk, gv = (nv_tensor_scales if nv_tensor_scales is not None
+                      else [nv_tensor_scale(t)[0] for t in (q, k, v)])
         fq_q = lambda x, axis: fake_quant_nv(x, axis, gq)   # noqa: E731
         fq_k = lambda x, axis: fake_quant_nv(x, axis, gk)   # noqa: E731
         fq_v = lambda x, axis: fake_quant_nv(x, axis, gv)   # noqa: E731

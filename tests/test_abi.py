@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert ops.attn_fp4_abi_version() == 5
+    assert ops.attn_fp4_abi_version() == 6
 
 
 def test_status_strings():
@@ -89,6 +89,40 @@ def test_host_validation_rejects_before_launch():
     need = L.attn_fp4_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     b = ops.BwdArgs(p, p, p, p, p, p, p, p, p, p, p, p, p, ctypes.c_void_p(1 << 20), need, B, Hq, Hkv, N, d, 0, 0.0)
     assert L.attn_fp4_bwd_recompute(ctypes.byref(b), None) == 3
+
+
+def test_nv_host_validation_rejects_before_launch():
+    L = ops.lib()
+    p = ctypes.c_void_p(256)
+    ts = ctypes.c_void_p(512)
+    # tensor scale missing or misaligned, d not a multiple of 32, axis 1 with n % 16, bad axis
+    assert L.attn_fp4_nv_quantize(p, 1, 32, 32, 0, p, p, None, None) == 1
+    assert L.attn_fp4_nv_quantize(p, 1, 32, 32, 0, p, p, ctypes.c_void_p(516), None) == 1
+    assert L.attn_fp4_nv_quantize(p, 1, 32, 48, 0, p, p, ts, None) == 1
+    assert L.attn_fp4_nv_quantize(p, 1, 40, 32, 1, p, p, ts, None) == 1
+    assert L.attn_fp4_nv_quantize(p, 1, 32, 32, 2, p, p, ts, None) == 1
+    assert L.attn_fp4_nv_quantize(ctypes.c_void_p(8), 1, 32, 32, 0, p, p, ts, None) == 1
+    # workspace: bf16 Q^ per query head, K^ and V^T per KV head, each region 256-aligned
+    assert L.attn_fp4_nv_fwd_workspace_bytes(1, 4, 2, 128, 64) == 4 * 128 * 64 * 2 + 2 * (2 * 128 * 64 * 2)
+    assert L.attn_fp4_nv_fwd_workspace_bytes(1, 4, 3, 128, 64) < 0
+    assert L.attn_fp4_nv_fwd(None, None) == 1
+    need = L.attn_fp4_nv_fwd_workspace_bytes(1, 4, 2, 128, 128)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def args(**kw):
+        a = dict(ts=ts, ws=ws, wsb=need, B=1, Hq=4, Hkv=2, N=128, d=128)
+        a.update(kw)
+        return ops.NvFwdArgs(p, p, p, p, p, p, a["ts"], a["ts"], a["ts"], p, p, p, a["ws"], a["wsb"],
+                             a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], 0, 0.0)
+    for kw in ({"N": 96}, {"d": 96}, {"Hkv": 3}, {"ts": None}, {"ts": ctypes.c_void_p(516)}):
+        assert L.attn_fp4_nv_fwd(ctypes.byref(args(**kw)), None) == 1, kw
+    assert L.attn_fp4_nv_fwd(ctypes.byref(args(ws=None)), None) == 5
+    assert L.attn_fp4_nv_fwd(ctypes.byref(args(wsb=need - 256)), None) == 5
+    assert L.attn_fp4_nv_fwd(ctypes.byref(args(ws=ctypes.c_void_p((1 << 20) + 16))), None) == 5
+    # one head's bf16 operand beyond 2^31 bytes: unsupported (32-bit buffer offsets)
+    big = 1 << 23
+    a = args(N=big, Hq=1, Hkv=1, wsb=L.attn_fp4_nv_fwd_workspace_bytes(1, 1, 1, big, 128))
+    assert L.attn_fp4_nv_fwd(ctypes.byref(a), None) == 3
 
 
 def test_binding_raises_without_library(monkeypatch):

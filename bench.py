@@ -8,9 +8,10 @@ HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
 Printed: one JSON line with the step throughput, a roofline object for the dominant kernel (the
 fused forward, timed alone with HIP events on the stream it runs on), the backward of the QAT
 workload (B=1, H=16, N=8192, d=128) measured the same way, the forward with the exp-free EFQ
-probability codes, the forward on the causal LLM and GQA-prefill workloads, the cache forward on
-a decode batch and a chunked-prefill step, and the CPU oracle timed on a bounded sample of the
-same workload.
+probability codes, the forward over NVFP4-style operands (E4M3 scale per 16 elements, bf16
+matrix core, fp16 operands) on the same inputs, the forward on the causal LLM and GQA-prefill workloads, the
+cache forward on a decode batch and a chunked-prefill step, and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 import argparse
@@ -25,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP4 attn fwd TFLOPS (4·B·H·N²·d) at N=32K,d=128; % of MXFP4 MFMA peak"
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak (published 10.1 PFLOP/s)
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published 8 TB/s)
 QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 
@@ -193,6 +194,42 @@ def bench_forward_configs(args, torch, ops, W):
     return out
 
 
+def bench_nvfp4(args, torch, ops, w, dev, reps=None):
+    """The NVFP4-style path on the same inputs: quantize Q, K (along d) and V (along the sequence) to
+    16-element blocks with E4M3 block scales and fp32 tensor scales, then the forward (its three
+    exact fp16 dequantization launches and the fp16 matrix-core attention kernel), each timed with
+    HIP events on its stream."""
+    stream = torch.cuda.current_stream()
+    B, H, N, d = w.B, w.Hq, w.N, w.d
+    quant = [ops.attn_fp4_nv_quantize(dev[t], 1 if t == "v" else 0) for t in ("q", "k", "v")]
+    (qc, qs, qt), (kc, ks, kt), (vc, vs, vt) = quant
+    ws = torch.empty(ops.attn_fp4_nv_fwd_workspace_bytes(B, H, H, N, d), dtype=torch.uint8, device="cuda")
+    o, m, l = ops.attn_fp4_nv_fwd(qc, qs, qt, kc, ks, kt, vc, vs, vt, causal=w.causal, workspace=ws)
+    fwd = lambda: ops.attn_fp4_nv_fwd(qc, qs, qt, kc, ks, kt, vc, vs, vt, causal=w.causal, o=o, m=m, l=l,
+                                      workspace=ws)
+    if reps:
+        for _ in range(reps):
+            fwd()
+        torch.cuda.synchronize()
+        return {"ran": reps}
+
+    def quantize():
+        for t, (c, sc, ts) in zip(("q", "k", "v"), quant):
+            ops.attn_fp4_nv_quantize(dev[t], 1 if t == "v" else 0, c, sc, ts)
+
+    for _ in range(2):
+        quantize()
+        fwd()
+    torch.cuda.synchronize()
+    ms = time_region(fwd, max(3, args.steps), stream)
+    qms = time_region(quantize, max(3, args.steps), stream)
+    flops = 4.0 * B * H * N * N * d
+    tf = flops / ms / 1e9
+    return {"ms_fwd": ms, "ms_quantize_qkv": qms, "tflops": tf, "frac_f16_mfma": tf / PEAK_BF16_TFLOPS,
+            "format": "E2M1, E4M3 scale per 16, fp32 tensor scale (a reading of NVFP4); fp16 matrix core",
+            "timed": "attn_fp4_nv_fwd entry point: three fp16 dequantization launches + the attention kernel"}
+
+
 def bench_kvcache(args, torch, ops, W, only=None):
     """The cache forward (attn_fp4_fwd_kvcache) on the decode and chunked-prefill workloads: the
     forward alone (K^/V^ already quantized in the cache), HIP events on its stream."""
@@ -251,6 +288,8 @@ def main():
                     help="if > 0: only run the QAT-workload backward this many times (for profilers)")
     ap.add_argument("--kv-only-reps", type=int, default=0,
                     help="if > 0: only run the decode cache forward this many times (for profilers)")
+    ap.add_argument("--nv-only-reps", type=int, default=0,
+                    help="if > 0: only run the NVFP4-style forward this many times (for profilers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="if > 0: only run a plain device copy of this many bytes 3 times "
                          "(calibrates the HBM byte counters of a profiler)")
@@ -315,6 +354,10 @@ def main():
         quantize()
         fwd()
 
+    if args.nv_only_reps > 0:
+        log("nvfp4", bench_nvfp4(args, torch, ops, w, dev, reps=args.nv_only_reps))
+        return
+
     if args.fwd_only_reps > 0:
         quantize()
         for _ in range(args.fwd_only_reps):
@@ -370,6 +413,8 @@ def main():
     }
     result["efq"] = {"ms": efq_ms, "tflops": flops / efq_ms / 1e9, "frac": flops / efq_ms / 1e9 / PEAK_FP4_TFLOPS,
                      "p_rule": "exp-free EFQ codes (a reading of the pages; not the headline definition)"}
+    result["nvfp4"] = bench_nvfp4(args, torch, ops, w, dev)
+    log("nvfp4", result["nvfp4"])
     del dev
     if not args.no_backward:
         result["backward"] = bench_backward(args, torch, ops, W)

@@ -274,7 +274,7 @@ int32_t attn_fp4_nv_fwd(const attn_fp4_nv_fwd_args* a, void* stream) {
   if (a->workspace == nullptr || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 ||
       a->workspace_bytes < ws.total)
     return ATTN_FP4_E_WORKSPACE;
-  // the kernel addresses one KV head's bf16 [N, d] operands with 32-bit buffer offsets
+  // the kernel addresses one KV head's fp16 [N, d] operands with 32-bit buffer offsets
   if (a->N * a->d * 2 > (int64_t)0x7FFFFFFF) return ATTN_FP4_E_UNSUPPORTED;
   st = check_device();
   if (st != ATTN_FP4_OK) return st;

@@ -76,12 +76,12 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d);
 
-// NVFP4-style forward: the operands dequantized to bf16 (E2M1 * E4M3 scale, exact) in the
+// NVFP4-style forward: the operands dequantized to fp16 (E2M1 * E4M3 scale, exact) in the
 // workspace, and the device-resident fp32 tensor scales.
 struct NvFwdParams {
-  const uint16_t* qb;   // Q^ / G_Q, bf16 [B, Hq, N, d]
-  const uint16_t* kb;   // K^ / G_K, bf16 [B, Hkv, N, d]
-  const uint16_t* vt;   // V^ / G_V transposed, bf16 [B, Hkv, d, N]
+  const uint16_t* qb;   // Q^ / G_Q, fp16 [B, Hq, N, d]
+  const uint16_t* kb;   // K^ / G_K, fp16 [B, Hkv, N, d]
+  const uint16_t* vt;   // V^ / G_V transposed, fp16 [B, Hkv, d, N]
   const float* q_ts;    // tensor scales G (first float of each attn_fp4_nv_quantize output)
   const float* k_ts;
   const float* v_ts;

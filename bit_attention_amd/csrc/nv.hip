@@ -10,10 +10,12 @@
 //   when S = 0); value = G * S * E2M1(code).
 //
 // gfx950's block-scaled matrix core takes power-of-two scales per 32 elements only, so this format
-// runs on the bf16 matrix core: the product of an E2M1 value (at most 2 significant bits) and an
+// runs on the fp16 matrix core: the product of an E2M1 value (at most 2 significant bits) and an
 // E4M3 scale (at most 4) has at most 6 significant bits and lies in [2^-10, 2688], so E2M1 * S is
-// exact in bf16, every bf16 product is exact in the fp32 accumulator, and the tensor scales are
-// applied once to the fp32 scores and outputs.
+// exact in fp16 (normal range 2^-14 .. 65504), every fp16 product is exact in the fp32
+// accumulator, and the tensor scales are applied once to the fp32 scores and outputs.  fp16
+// rather than bf16 because its packed multiply and dot instructions let the probabilities be
+// rebuilt two at a time.
 //
 // The probabilities are requantized in the same format per 16 keys (the tensor scale of P is the
 // one for amax = 1, as p <= 1 with equality at the row maximum): S = E4M3(max p * 448), P~ =
@@ -28,10 +30,19 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNvDiv = 2688.0f;
+constexpr float kLog2NvDiv = 11.392317422778760f;    // log2(2688)
 constexpr float kNvGMin = 6.018531076210112e-36f;   // 2^-117
 
-__device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v16f mfma_f16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+
+// Two fp32 values that are exact in fp16 -> packed fp16.
+__device__ __forceinline__ uint32_t pk_f16_exact(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 // Nearest E4M3 value to t >= 0 (finite), ties to the even mantissa, saturating at 448.  The
@@ -162,7 +173,7 @@ __global__ void __launch_bounds__(256) nv_quantize_cols_kernel(const uint32_t* _
   scales[row * (n / 16) + tb] = (uint8_t)e4m3_byte(S);
 }
 
-// ---- dequantize to bf16 (E2M1 * S, exact; the tensor scale is applied by the consumer) --------
+// ---- dequantize to fp16 (E2M1 * S, exact; the tensor scale is applied by the consumer) --------
 // Flat over 32-element units: 16 code bytes, 2 scale bytes -> 64 output bytes.
 __global__ void __launch_bounds__(256) nv_dequant_kernel(const uint4* __restrict__ codes, const uint16_t* __restrict__ scales,
                                                          uint4* __restrict__ out, int64_t units) {
@@ -180,10 +191,10 @@ __global__ void __launch_bounds__(256) nv_dequant_kernel(const uint4* __restrict
       const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 1);
       const v2f e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 2);
       const v2f h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 3);
-      o[4 * q + 0] = pk_bf16(a[0] * s, a[1] * s);
-      o[4 * q + 1] = pk_bf16(b[0] * s, b[1] * s);
-      o[4 * q + 2] = pk_bf16(e[0] * s, e[1] * s);
-      o[4 * q + 3] = pk_bf16(h[0] * s, h[1] * s);
+      o[4 * q + 0] = pk_f16_exact(a[0] * s, a[1] * s);
+      o[4 * q + 1] = pk_f16_exact(b[0] * s, b[1] * s);
+      o[4 * q + 2] = pk_f16_exact(e[0] * s, e[1] * s);
+      o[4 * q + 3] = pk_f16_exact(h[0] * s, h[1] * s);
     }
     uint4* dst = out + 4 * u;
     dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -195,11 +206,11 @@ __global__ void __launch_bounds__(256) nv_dequant_kernel(const uint4* __restrict
 
 // ---- forward ----------------------------------------------------------------------------------
 // Workgroup = W waves of 32 query rows; key tiles of 64 staged in LDS by direct global -> LDS
-// loads, two stages, one tile ahead.  S^T = K^ Q^T and O^T += V^T P~^T on the bf16 matrix core.
+// loads, two stages, one tile ahead.  S^T = K^ Q^T and O^T += V^T P~^T on the fp16 matrix core.
 template <int D>
 struct NvLds {
-  static constexpr int KB = 0;                        // K^ bf16 [64 slots][D], swizzled chunks
-  static constexpr int VT = KB + 64 * D * 2;          // V^T bf16 [D][64 keys], swizzled chunks
+  static constexpr int KB = 0;                        // K^ fp16 [64 slots][D], swizzled chunks
+  static constexpr int VT = KB + 64 * D * 2;          // V^T fp16 [D][64 keys], swizzled chunks
   static constexpr int BYTES = VT + D * 64 * 2;
 };
 
@@ -209,7 +220,7 @@ nv_fwd_kernel(NvFwdParams p) {
   using L = NvLds<D>;
   constexpr int DS_STEPS = D / 16;
   constexpr int CT = D / 32;
-  constexpr int VC = D / 8;               // 16-B chunks per K^ bf16 row
+  constexpr int VC = D / 8;               // 16-B chunks per K^ fp16 row
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::BYTES];
 
   const int tid = threadIdx.x;
@@ -239,7 +250,7 @@ nv_fwd_kernel(NvFwdParams p) {
   const float snat = p.scale_nat * gq * gk;   // raw score -> natural-log units
   const float c = snat * kLog2e;              // raw score -> base-2 exponent
 
-  // the wave's Q^ rows (bf16 B operand of S^T), fixed for the kernel
+  // the wave's Q^ rows (fp16 B operand of S^T), fixed for the kernel
   v4i qf[DS_STEPS];
   {
     const uint16_t* qr = p.qb + (bh * N + row) * D;
@@ -309,7 +320,7 @@ nv_fwd_kernel(NvFwdParams p) {
       for (int s = 0; s < DS_STEPS; ++s) {
         const int cc = 2 * s + hi;
         const v4i a = *reinterpret_cast<const v4i*>(base + L::KB + slot * 2 * D + 16 * (cc ^ swz_big(slot, VC)));
-        st[T] = mfma_bf16(a, qf[s], st[T]);
+        st[T] = mfma_f16(a, qf[s], st[T]);
       }
       if (CAUSAL && ((int64_t)t * 64 + 63 > qw)) {
         const int jrel = (int)(row - (int64_t)t * 64) - 32 * T - 16 * hi;
@@ -346,23 +357,28 @@ nv_fwd_kernel(NvFwdParams p) {
         for (int r = 0; r < 16; ++r) acc[ct][r] *= alpha;
       lsum *= alpha;
     }
-    // P~ per block: S = E4M3(max p * 448), P~ 2688 = E2M1(p 2688 / S) S (bf16, exact)
+    // P~ per block: S = E4M3(max p * 448), P~ 2688 = E2M1(v) S with v = p 2688 / S (fp16, exact).
+    // v = 2^(s c - mc + log2(2688 / S)): the division by S rides on the exponential.  With
+    // S = 2^k mu (mu in [1, 2)), the decode to fp16 applies 2^k (the convert takes only the
+    // exponent of its scale operand) and one packed multiply applies mu to two values.
     uint32_t pw[2][8];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       const float bp = __builtin_amdgcn_exp2f(__builtin_fmaf(bm[T], c, -mc));
       const float S = e4m3_round(bp * 448.0f);
-      const float rs = S > 0.0f ? kNvDiv * __builtin_amdgcn_rcpf(S) : 0.0f;
+      const float sh = S > 0.0f ? mc - (kLog2NvDiv - __builtin_amdgcn_logf(S)) : __builtin_inff();
+      const _Float16 mu = (_Float16)__uint_as_float((__float_as_uint(S) & 0x007FFFFFu) | 0x3F800000u);
+      const v2h mu2 = {mu, mu};
+      const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
       float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][r], c, -mc)) * rs;
+      for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[T][r], c, -sh));
       const uint32_t c0 = e2m1_pack8(v), c1 = e2m1_pack8(v + 8);
       static_for<8>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
-        const v2f d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q < 4 ? c0 : c1, 1.0f, q & 3);
-        const float x0 = d2[0] * S, x1 = d2[1] * S;
-        lsum += x0 + x1;
-        pw[T][q] = pk_bf16(x0, x1);
+        const v2h x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q < 4 ? c0 : c1, S, q & 3) * mu2;
+        lsum = __builtin_amdgcn_fdot2(x, ones, lsum, false);
+        pw[T][q] = __builtin_bit_cast(uint32_t, x);
       });
     }
     // O^T += V^T P~^T: k-step s2 of half T takes keys 32T + 16hi + 8s2 + [0, 8) (registers 8s2..)
@@ -376,7 +392,7 @@ nv_fwd_kernel(NvFwdParams p) {
         for (int ct = 0; ct < CT; ++ct) {
           const int ch = 32 * ct + l32;
           const v4i a = *reinterpret_cast<const v4i*>(base + L::VT + ch * 128 + 16 * (cc ^ swz_big(ch, 8)));
-          acc[ct] = mfma_bf16(a, bsv, acc[ct]);
+          acc[ct] = mfma_f16(a, bsv, acc[ct]);
         }
       }
   };

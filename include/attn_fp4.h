@@ -303,7 +303,7 @@ int32_t attn_fp4_nv_quantize(const void* x, int64_t bh, int64_t n, int64_t d, in
  *   probability units).
  *   workspace: device memory, 256-byte aligned, of at least
  *   attn_fp4_nv_fwd_workspace_bytes(...) bytes (the operands dequantized to
- *   bf16); contents on entry do not matter and are clobbered.
+ *   fp16); contents on entry do not matter and are clobbered.
  */
 typedef struct {
   const void* q_codes;
@@ -334,11 +334,12 @@ int64_t attn_fp4_nv_fwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int6
  * NVFP4-style operands.  P is requantized per 16 keys in the same format with
  * the tensor scale of amax = 1: S = E4M3(max p * 448), P~ = E2M1(p * 2688 / S)
  * * S / 2688.  gfx950's block-scaled matrix core takes power-of-two scales per
- * 32 elements only, so both products run on the bf16 matrix core, where
- * E2M1 * E4M3 values are exact; fp32 accumulation and softmax state.
+ * 32 elements only, so both products run on the fp16 matrix core, where
+ * E2M1 * E4M3 values (at most 6 significant bits, within 2^-10 .. 2688) are
+ * exact; fp32 accumulation and softmax state; O is bf16.
  * Supported: d == 128 or d == 64, N % 64 == 0, Hq % Hkv == 0.
  * Errors: ATTN_FP4_E_INVALID_ARG, ATTN_FP4_E_WORKSPACE,
- * ATTN_FP4_E_UNSUPPORTED (N * d * 2 above 2^31 - 1: one head's bf16 operand
+ * ATTN_FP4_E_UNSUPPORTED (N * d * 2 above 2^31 - 1: one head's fp16 operand
  * exceeds the kernel's 32-bit buffer offsets), ATTN_FP4_E_UNSUPPORTED_DEVICE,
  * ATTN_FP4_E_HIP.
  */

@@ -102,7 +102,7 @@ def test_nv_host_validation_rejects_before_launch():
     assert L.attn_fp4_nv_quantize(p, 1, 40, 32, 1, p, p, ts, None) == 1
     assert L.attn_fp4_nv_quantize(p, 1, 32, 32, 2, p, p, ts, None) == 1
     assert L.attn_fp4_nv_quantize(ctypes.c_void_p(8), 1, 32, 32, 0, p, p, ts, None) == 1
-    # workspace: bf16 Q^ per query head, K^ and V^T per KV head, each region 256-aligned
+    # workspace: fp16 Q^ per query head, K^ and V^T per KV head, each region 256-aligned
     assert L.attn_fp4_nv_fwd_workspace_bytes(1, 4, 2, 128, 64) == 4 * 128 * 64 * 2 + 2 * (2 * 128 * 64 * 2)
     assert L.attn_fp4_nv_fwd_workspace_bytes(1, 4, 3, 128, 64) < 0
     assert L.attn_fp4_nv_fwd(None, None) == 1

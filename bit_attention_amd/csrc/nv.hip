@@ -85,17 +85,29 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float* v) {
 __global__ void nv_amax_clear_kernel(float* ts) { reinterpret_cast<uint32_t*>(ts)[1] = 0u; }
 
 // Largest |x| over the tensor into ts[1] (fp32 bits; non-negative floats order as unsigned ints).
+// Four 16-byte loads in flight per lane; one atomic per workgroup.
+__device__ __forceinline__ uint32_t bf16x8_absmax(uint4 w) {
+  const uint32_t m0 = max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu), max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu));
+  const uint32_t m1 = max(max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu), max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu));
+  return max(m0, m1);
+}
+
 __global__ void __launch_bounds__(256) nv_amax_kernel(const uint4* __restrict__ x, int64_t n8, float* ts) {
+  __shared__ uint32_t wmax[4];
   uint32_t a = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const uint4 w = x[i];
-    a = max(a, max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu), max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu)));
-    a = max(a, max(max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu), max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu)));
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * T < n8; i += 4 * T) {
+    const uint4 w0 = x[i], w1 = x[i + T], w2 = x[i + 2 * T], w3 = x[i + 3 * T];
+    a = max(a, max(max(bf16x8_absmax(w0), bf16x8_absmax(w1)), max(bf16x8_absmax(w2), bf16x8_absmax(w3))));
   }
+  for (; i < n8; i += T) a = max(a, bf16x8_absmax(x[i]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<uint32_t*>(ts) + 1, a << 16);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(reinterpret_cast<uint32_t*>(ts) + 1, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16);
 }
 
 // ---- axis 0 (Q, K): blocks along the contiguous last axis ----------------------------------
@@ -459,7 +471,8 @@ hipError_t launch_nv_quantize(const void* x, int64_t bh, int64_t n, int64_t d, i
                               float* ts, hipStream_t stream) {
   const int64_t n8 = bh * n * d / 8;
   hipLaunchKernelGGL(nv_amax_clear_kernel, dim3(1), dim3(1), 0, stream, ts);
-  hipLaunchKernelGGL(nv_amax_kernel, dim3(min(grid_for(n8), 2048u)), dim3(256), 0, stream, (const uint4*)x, n8, ts);
+  hipLaunchKernelGGL(nv_amax_kernel, dim3(min(grid_for((n8 + 3) / 4), 2048u)), dim3(256), 0, stream, (const uint4*)x,
+                     n8, ts);
   if (axis == 0) {
     hipLaunchKernelGGL(nv_quantize_rows_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, (const uint4*)x,
                        (uint32_t*)codes, (uint8_t*)scales, ts, n8);

@@ -88,3 +88,41 @@ def test_split_decode_graph_replays():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(m, ref[1]) and torch.equal(l, ref[2]), r
+
+
+def test_nvfp4_quantize_and_forward_graph_replays():
+    # the tensor amax is cleared by a kernel, not a memset, so the NVFP4-style path captures too
+    import torch
+    from bit_attention_amd import ops
+    B, Hq, Hkv, N, d = 1, 4, 2, 512, 128
+    q, k, v = rand_bf16((B, Hq, N, d), 7, 1.3), rand_bf16((B, Hkv, N, d), 8), rand_bf16((B, Hkv, N, d), 9)
+    qq, kq, vq = ops.attn_fp4_nv_quantize(q, 0), ops.attn_fp4_nv_quantize(k, 0), ops.attn_fp4_nv_quantize(v, 1)
+    ws = torch.empty(ops.attn_fp4_nv_fwd_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device="cuda")
+    m = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+
+    def step():
+        for x, axis, out in ((q, 0, qq), (k, 0, kq), (v, 1, vq)):
+            ops.attn_fp4_nv_quantize(x, axis, *out)
+        ops.attn_fp4_nv_fwd(*qq, *kq, *vq, causal=True, o=o, m=m, l=l, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), m.clone(), l.clone(), qq[2].clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        o.zero_(); m.zero_(); l.zero_(); ws.zero_(); qq[2].fill_(7.0)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(m, ref[1]) and torch.equal(l, ref[2]), r
+        assert torch.equal(qq[2], ref[3]), r

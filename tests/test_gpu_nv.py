@@ -164,3 +164,23 @@ def test_forward_full_size_sampled(name):
     rows = W.sample_rows(w.N, count=256)
     heads = [(0, 0), (w.B - 1, w.Hq - 1)]
     check_fwd(q, k, v, w.causal, o, m, l, heads, rows, name)
+
+
+def test_forward_workspace_reuse_and_smaller_second_call():
+    # one workspace serves a large call and then a smaller one; the second must not see the first
+    import torch
+    from bit_attention_amd import ops
+    rng = np.random.default_rng(12)
+    big = [bf16(rng.standard_normal((1, 4, 512, 128))) for _ in range(3)]
+    small = [bf16(rng.standard_normal((1, 2, 128, 128)) * 2) for _ in range(3)]
+    ws = torch.empty(ops.attn_fp4_nv_fwd_workspace_bytes(1, 4, 4, 512, 128), dtype=torch.uint8, device="cuda")
+    outs = []
+    for q, k, v in (big, small):
+        qq = ops.attn_fp4_nv_quantize(to_dev(q, torch.bfloat16), 0)
+        kq = ops.attn_fp4_nv_quantize(to_dev(k, torch.bfloat16), 0)
+        vq = ops.attn_fp4_nv_quantize(to_dev(v, torch.bfloat16), 1)
+        o, m, l = ops.attn_fp4_nv_fwd(*qq, *kq, *vq, causal=False, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.float().cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()))
+    q, k, v = small
+    check_fwd(q, k, v, False, *outs[1], [(0, 0), (0, 1)], np.arange(128), "second call")

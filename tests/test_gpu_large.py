@@ -1,6 +1,6 @@
-"""Parity at the largest sizes this suite runs: a 131072-token head through the forward, a
-131072-key decode through the split cache forward, and a 2^27-element quantization, each
-launched whole and compared with the oracle on sampled rows, heads or blocks (rows, heads and
+"""Parity at the largest sizes this suite runs: a 131072-token head through the forward (MXFP4 and
+NVFP4-style), a 131072-key decode through the split cache forward, and a 2^27-element
+quantization, each launched whole and compared with the oracle on sampled rows, heads or blocks (rows, heads and
 blocks are independent, so each sample is exact parity)."""
 
 import numpy as np
@@ -84,3 +84,26 @@ def test_quantize_2_27_elements_sampled(axis):
             packed = oracle.pack_nibbles(rc, -1).reshape(d, 64, 16).swapaxes(0, 1)   # [64 blocks, d, 16]
             assert np.array_equal(s[h, blk:blk + 64].cpu().numpy(), rs.T)
             assert np.array_equal(c[h, blk:blk + 64].cpu().numpy(), packed)
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_nvfp4_forward_131072_tokens_sampled_rows(d, causal):
+    # the NVFP4-style path at the same length: tensor scales over the whole tensors, sampled rows
+    import torch
+    from bit_attention_amd import ops
+    N = 131072
+    q = rand_bf16((1, 1, N, d), 8200 + d + causal, 1.2)
+    k = rand_bf16((1, 1, N, d), 8202)
+    v = rand_bf16((1, 1, N, d), 8203)
+    qq, kq, vq = (ops.attn_fp4_nv_quantize(to_dev(x, torch.bfloat16), ax) for x, ax in ((q, 0), (k, 0), (v, 1)))
+    o, m, l = ops.attn_fp4_nv_fwd(*qq, *kq, *vq, causal=causal)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 4095, 65536, 99999, N - 65, N - 2, N - 1])
+    o = o[0, 0, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    m = m[0, 0].cpu().numpy()[rows]
+    l = l[0, 0].cpu().numpy()[rows]
+    scales = tuple(oracle.nv_tensor_scale(t)[0] for t in (q, k, v))
+    ro, rm, rl = oracle.attn_fwd(q, k, v, causal=causal, rows=rows, fmt="nv", nv_tensor_scales=scales)
+    compare(o, ro[0, 0], "NVFP4 N=131072 O")
+    assert np.max(np.abs(m - rm[0, 0])) <= 1e-5 * max(1.0, np.abs(rm).max())
+    compare(l, rl[0, 0], "NVFP4 N=131072 l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())

@@ -772,7 +772,10 @@ bwd_dkdv_ws_kernel(BwdParams p) {
                                                                    ksc[kt], 0, qsc);
           st = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka[kt][1]), widen(q1v), st, 4, 4, 2, ksc[kt], 2,
                                                                qsc);
-          v16f dp = v16f{};
+          // dP^T - D/l: the accumulator starts at -D/l, so dS needs one multiply per element
+          v16f dp;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = -ddl;
 #pragma unroll
           for (int s = 0; s < 8; ++s) dp = mfma_bf16(va[kt][s], dov[s], dp);
           // register r holds key kp + 16 hi + r
@@ -800,8 +803,8 @@ bwd_dkdv_ws_kernel(BwdParams p) {
             u = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u, pr[4 * q + 2], pr[4 * q + 3], sc, 1);
             aw[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 0));
             aw[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, sc, 1));
-            sw8[2 * q] = pk_bf16(pr[4 * q] * (dp[4 * q] - ddl), pr[4 * q + 1] * (dp[4 * q + 1] - ddl));
-            sw8[2 * q + 1] = pk_bf16(pr[4 * q + 2] * (dp[4 * q + 2] - ddl), pr[4 * q + 3] * (dp[4 * q + 3] - ddl));
+            sw8[2 * q] = pk_bf16(pr[4 * q] * dp[4 * q], pr[4 * q + 1] * dp[4 * q + 1]);
+            sw8[2 * q + 1] = pk_bf16(pr[4 * q + 2] * dp[4 * q + 2], pr[4 * q + 3] * dp[4 * q + 3]);
           }
           outp[kt][0] = v4i{(int)aw[0], (int)aw[1], (int)aw[2], (int)aw[3]};
           outp[kt][1] = v4i{(int)aw[4], (int)aw[5], (int)aw[6], (int)aw[7]};

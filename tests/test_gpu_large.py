@@ -1,6 +1,6 @@
 """Parity at the largest sizes this suite runs: a 131072-token head through the forward (MXFP4 and
 NVFP4-style), a 131072-key decode through the split cache forward, and a 2^27-element
-quantization, each launched whole and compared with the oracle on sampled rows, heads or blocks
+quantization (both formats), each launched whole and compared with the oracle on sampled rows, heads or blocks
 (rows, heads and blocks are independent, so each sample is exact parity)."""
 
 import numpy as np
@@ -107,3 +107,32 @@ def test_nvfp4_forward_131072_tokens_sampled_rows(d, causal):
     compare(o, ro[0, 0], "NVFP4 N=131072 O")
     assert np.max(np.abs(m - rm[0, 0])) <= 1e-5 * max(1.0, np.abs(rm).max())
     compare(l, rl[0, 0], "NVFP4 N=131072 l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_nvfp4_quantize_2_27_elements_sampled(axis):
+    # the tensor scale comes from the whole 2^27-element tensor (amax on the device, checked here
+    # against the host's); codes and scales of sampled 2048-token slices are bit-exact
+    import torch
+    from bit_attention_amd import ops
+    bh, n, d = 8, 131072, 128
+    x = torch.randn(bh, n, d, device="cuda", dtype=torch.float32).mul_(3.0).to(torch.bfloat16)
+    c, s, ts = ops.attn_fp4_nv_quantize(x, axis)
+    torch.cuda.synchronize()
+    amax = float(x.abs().max().float().cpu())
+    g, _ = oracle.nv_tensor_scale(np.array([amax]))
+    tsh = ts.cpu().numpy()
+    assert tsh[1] == np.float32(amax) and tsh[0] == g
+    r = np.random.default_rng(8130 + axis)
+    for h in r.choice(bh, 2, replace=False):
+        blk = int(r.integers(0, n // 16 - 128))
+        rows = slice(16 * blk, 16 * blk + 2048)       # 128 whole blocks of 16 tokens
+        xs = x[h, rows].float().cpu().numpy()
+        if axis == 0:
+            rc, rs, _ = oracle.quantize_nv(xs, axis=-1, g=g)
+            assert np.array_equal(s[h, rows].cpu().numpy(), rs)
+            assert np.array_equal(c[h, rows].cpu().numpy(), oracle.pack_nibbles(rc, -1))
+        else:
+            rc, rs, _ = oracle.quantize_nv(xs.T, axis=-1, g=g)              # [d, 2048]
+            assert np.array_equal(s[h, :, blk:blk + 128].cpu().numpy(), rs)
+            assert np.array_equal(c[h, :, 8 * blk:8 * blk + 1024].cpu().numpy(), oracle.pack_nibbles(rc, -1))

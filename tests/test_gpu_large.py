@@ -1,7 +1,7 @@
 """Parity at the largest sizes this suite runs: a 131072-token head through the forward (MXFP4 and
 NVFP4-style), a 131072-key decode through the split cache forward, and a 2^27-element
-quantization (both formats), each launched whole and compared with the oracle on sampled rows, heads or blocks
-(rows, heads and blocks are independent, so each sample is exact parity)."""
+quantization (both formats), each launched whole and compared with the oracle on sampled rows,
+heads or blocks (rows, heads and blocks are independent, so each sample is exact parity)."""
 
 import numpy as np
 import pytest

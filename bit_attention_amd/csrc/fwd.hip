@@ -329,7 +329,8 @@ fwd_kernel(FwdParams p) {
     const float m_new = fmaxf(m_run, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
     // a row that has seen no key yet keeps m = -inf; its shift is taken as 0 (alpha = 0, p = 0)
     const float m_sh = KV ? (m_new == -__builtin_inff() ? 0.0f : m_new) : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_sh) * c);
+    const float m_prev = m_run;
+    const bool raised = m_new != m_prev;          // else alpha = exp2(0) = 1: nothing to rescale
     m_run = m_new;
     // E8M0 scale of the block from its max p = exp2((bm - m) c): the biased exponent of p is
     // floor((bm - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
@@ -379,8 +380,9 @@ fwd_kernel(FwdParams p) {
     }
     const v8i pb = v8i{(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1], 0, 0, 0, 0};
 
-    // history rescale (skipped when no row of the wave raised its max)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    // history rescale (skipped, with its exp, when no row of the wave raised its max)
+    if (__builtin_amdgcn_ballot_w64(raised) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f((m_prev - m_sh) * c);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

@@ -359,10 +359,12 @@ nv_fwd_kernel(NvFwdParams p) {
     }
     const float mraw_new = fmaxf(mraw, mt);
     const float mc_new = mraw_new * c;
-    const float alpha = __builtin_amdgcn_exp2f(mc - mc_new);
+    const float mc_prev = mc;
+    const bool raised = mraw_new != mraw;         // else alpha = exp2(0) = 1: nothing to rescale
     mraw = mraw_new;
     mc = mc_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    if (__builtin_amdgcn_ballot_w64(raised)) {
+      const float alpha = __builtin_amdgcn_exp2f(mc_prev - mc_new);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

@@ -186,33 +186,28 @@ __global__ void __launch_bounds__(256) nv_quantize_cols_kernel(const uint32_t* _
 }
 
 // ---- dequantize to fp16 (E2M1 * S, exact; the tensor scale is applied by the consumer) --------
-// Flat over 32-element units: 16 code bytes, 2 scale bytes -> 64 output bytes.
-__global__ void __launch_bounds__(256) nv_dequant_kernel(const uint4* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                                         uint4* __restrict__ out, int64_t units) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const uint4 c = codes[u];
-    const uint32_t sw = scales[u];
-    const float s0 = e4m3_value(sw & 0xFF), s1 = e4m3_value(sw >> 8);
-    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    uint32_t o[16];
+// Flat over 8-element chunks (one code dword, half a scale byte, 16 output bytes).  Lane l of a
+// wave takes chunks 64 j + l of the wave's 256, so that every load and store instruction of the
+// wave covers one contiguous run.
+__global__ void __launch_bounds__(256) nv_dequant_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                         uint4* __restrict__ out, int64_t chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); w * 256 < chunks; w += waves) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float s = q < 2 ? s0 : s1;
-      const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 0);
-      const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 1);
-      const v2f e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 2);
-      const v2f h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 3);
-      o[4 * q + 0] = pk_f16_exact(a[0] * s, a[1] * s);
-      o[4 * q + 1] = pk_f16_exact(b[0] * s, b[1] * s);
-      o[4 * q + 2] = pk_f16_exact(e[0] * s, e[1] * s);
-      o[4 * q + 3] = pk_f16_exact(h[0] * s, h[1] * s);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = w * 256 + 64 * j + lane;
+      if (c < chunks) {
+        const uint32_t cw = codes[c];
+        const float s = e4m3_value(scales[c >> 1]);
+        const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+        const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+        const v2f e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+        const v2f h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+        out[c] = make_uint4(pk_f16_exact(a[0] * s, a[1] * s), pk_f16_exact(b[0] * s, b[1] * s),
+                            pk_f16_exact(e[0] * s, e[1] * s), pk_f16_exact(h[0] * s, h[1] * s));
+      }
     }
-    uint4* dst = out + 4 * u;
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
   }
 }
 
@@ -498,13 +493,13 @@ NvWorkspace nv_fwd_workspace_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t 
 hipError_t launch_nv_fwd(const NvFwdParams& p, const void* q_codes, const void* q_scales, const void* k_codes,
                          const void* k_scales, const void* v_codes, const void* v_scales, int d, bool causal,
                          hipStream_t stream) {
-  struct Job { const void* c; const void* s; const uint16_t* out; int64_t units; };
-  const Job jobs[3] = {{q_codes, q_scales, p.qb, p.B * p.Hq * p.N * d / 32},
-                       {k_codes, k_scales, p.kb, p.B * p.Hkv * p.N * d / 32},
-                       {v_codes, v_scales, p.vt, p.B * p.Hkv * p.N * d / 32}};
+  struct Job { const void* c; const void* s; const uint16_t* out; int64_t chunks; };
+  const Job jobs[3] = {{q_codes, q_scales, p.qb, p.B * p.Hq * p.N * d / 8},
+                       {k_codes, k_scales, p.kb, p.B * p.Hkv * p.N * d / 8},
+                       {v_codes, v_scales, p.vt, p.B * p.Hkv * p.N * d / 8}};
   for (const Job& j : jobs)
-    hipLaunchKernelGGL(nv_dequant_kernel, dim3(grid_for(j.units)), dim3(256), 0, stream, (const uint4*)j.c,
-                       (const uint16_t*)j.s, (uint4*)const_cast<uint16_t*>(j.out), j.units);
+    hipLaunchKernelGGL(nv_dequant_kernel, dim3(grid_for((j.chunks + 3) / 4)), dim3(256), 0, stream, (const uint32_t*)j.c,
+                       (const uint8_t*)j.s, (uint4*)const_cast<uint16_t*>(j.out), j.chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d == 128) return causal ? launch_nv_fwd_d<128, true>(p, stream) : launch_nv_fwd_d<128, false>(p, stream);

@@ -54,6 +54,10 @@ quantizers on -> the direct formula; Q = 0 -> mean of V^ (causal: prefix
 mean); identical V^ rows -> that row; V -> 2^k V scales O exactly;
 quantizers off -> float64 autograd of textbook attention and central finite
 differences; Q = 0 with quantizers on -> autograd at (Q^, K^, V^);
+quantizers on with all keys in one tile (so that the forward's running max
+is the final row max) -> float64 autograd of the fake-quant forward with
+straight-through Q^, K^, V^, P~ and a constant row max, causal, GQA, d = 64
+and 128 (this fixes which of P, P~ and MXFP4(P) feeds dV and dS);
 D = rowsum(P o dP) with quantizers off.  Cache forward
 (tests/test_oracle_kvcache.py): quantizers off -> textbook attention over
 the visible keys; quantizers on -> rows of the full forward at those

@@ -208,3 +208,86 @@ def test_row_max_equals_forward_final_max(causal):
     q, k, v = rand((1, 4, 192, 32), 40, 2.0), rand((1, 2, 192, 32), 41), rand((1, 2, 192, 32), 42)
     _, m, _ = attn_fwd(q, k, v, causal=causal)
     assert np.array_equal(attn_row_max(q, k, causal=causal, chunk=50), m)
+
+
+def _fq_torch(x, axis):
+    """MXFP4 fake quantization of a float64 tensor's values (the oracle's quantizer, pinned in
+    tests/test_oracle_mx.py), as a constant: gradients are attached by the caller."""
+    return torch.from_numpy(fake_quant_mx(x.detach().numpy(), axis))
+
+
+def _ste(x, axis):
+    # straight-through estimator: forward value Q(x), gradient of the identity
+    return x + (_fq_torch(x, axis) - x).detach()
+
+
+def ste_single_tile_grads(q, k, v, do, causal):
+    """float64 autograd of the fake-quant forward with all keys in one tile.
+
+    Q^, K^ (along d), V^ (along the sequence) and P~ (along the keys, per 32) pass gradients
+    straight through; the row max is a constant.  With one tile the forward's running max is the
+    final row max, so its P~ = MXFP4(exp(s - m)) is exactly the one the backward requantizes.
+    Returns O and the gradients of sum(O * dO) with respect to q, k, v.
+    """
+    tq, tk, tv = (torch.tensor(t, dtype=torch.float64, requires_grad=True) for t in (q, k, v))
+    B, Hq, N, d = q.shape
+    group = Hq // k.shape[1]
+    qh = _ste(tq, -1)
+    kh = _ste(tk, -1).repeat_interleave(group, dim=1)
+    vh = _ste(tv, -2).repeat_interleave(group, dim=1)
+    s = torch.matmul(qh, kh.transpose(-1, -2).contiguous()) / np.sqrt(d)
+    if causal:
+        s = s.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+    m = s.max(dim=-1, keepdim=True).values.detach()
+    p = torch.exp(s - m)
+    pt = _ste(p, -1)
+    l = pt.sum(dim=-1, keepdim=True)
+    o = torch.matmul(pt, vh) / l
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+STE_CASES = [(False, 1, 1, 64, 64), (False, 2, 2, 128, 128), (True, 2, 2, 256, 64),
+             (True, 4, 2, 128, 128), (False, 4, 2, 256, 128), (True, 2, 1, 64, 128)]
+
+
+@pytest.mark.parametrize("causal,hq,hkv,n,d", STE_CASES)
+def test_backward_quantized_equals_ste_autograd(causal, hq, hkv, n, d):
+    """Attn-QAT abstract, principles (1) and (2): the backward recomputes the FP4 scores and
+    feeds P~ = MXFP4(p)/l to dV, the unquantized P to dS, and the FP4 forward's own O to D.
+    With one key tile that is exactly the straight-through gradient of the fake-quant forward."""
+    seed = 50 + n + d + 7 * hq + causal
+    q, k, v = rand((1, hq, n, d), seed, 2.0), rand((1, hkv, n, d), seed + 1, 1.5), rand((1, hkv, n, d), seed + 2)
+    do = rand((1, hq, n, d), seed + 3)
+    o, m, l = attn_fwd(q, k, v, causal=causal, bc=n)      # one tile: running max = final max
+    ro, gq, gk, gv = ste_single_tile_grads(q, k, v, do, causal)
+    assert np.max(np.abs(o - ro)) < 1e-12
+    dq, dk, dv = attn_bwd(q, k, v, o, do, m, l, causal=causal, chunk=40)
+    for a, b in ((dq, gq), (dk, gk), (dv, gv)):
+        assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+
+def test_ste_pin_rejects_plausible_backward_mistakes():
+    """The autograd pin separates the oracle's placement of P~ from three plausible mistakes:
+    dV from the unquantized P, dV from MXFP4(P) (quantizing p / l instead of p), and P~/l in dS.
+    Each mistake is written out here on one head; each misses the autograd gradient by far more
+    than the 1e-12 the oracle meets."""
+    n, d = 128, 64
+    q, k, v = rand((1, 1, n, d), 90, 2.0), rand((1, 1, n, d), 91, 1.5), rand((1, 1, n, d), 92)
+    do = rand((1, 1, n, d), 93)
+    o, m, l = attn_fwd(q, k, v, bc=n)
+    _, gq, gk, gv = ste_single_tile_grads(q, k, v, do, False)
+    qh, kh, vh = fake_quant_mx(q[0, 0], -1), fake_quant_mx(k[0, 0], -1), fake_quant_mx(v[0, 0], 0)
+    s = qh @ kh.T / np.sqrt(d)
+    p = np.exp(s - m[0, 0][:, None])
+    P = p / l[0, 0][:, None]
+    Pt = fake_quant_mx(p, -1) / l[0, 0][:, None]
+    D = np.sum(do[0, 0] * o[0, 0], axis=1)
+    dP = do[0, 0] @ vh.T
+    dv_a, dv_b = P.T @ do[0, 0], fake_quant_mx(P, -1).T @ do[0, 0]
+    dk_c = (Pt * (dP - D[:, None])).T @ qh / np.sqrt(d)
+    dk_ok = (P * (dP - D[:, None])).T @ qh / np.sqrt(d)
+    assert np.max(np.abs(dk_ok - gk[0, 0])) < 1e-12          # the oracle's own placement
+    assert np.max(np.abs(Pt.T @ do[0, 0] - gv[0, 0])) < 1e-12
+    for bad, good in ((dv_a, gv), (dv_b, gv), (dk_c, gk)):
+        assert np.max(np.abs(bad - good[0, 0])) > 1e-3

@@ -107,36 +107,170 @@ def time_region(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(w, seconds_target=15.0):
-    """The oracle, untouched, on a bounded sample of the same workload (one head, sampled rows)."""
+_ONE_THREAD_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
+def _cpu_worker_init():
+    # one BLAS thread per worker process: the pool itself spreads the work over the cores (the
+    # environment set at spawn covers the BLAS loaded by numpy; the limit covers any loaded later)
+    import numpy  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _cpu_task(a):
+    """Oracle forward of some query rows of one head (fresh process: numpy only, no GPU state)."""
     import numpy as np
     import oracle
     from bit_attention_amd import workloads as W
+    name, b, h, rows = a
+    w = W.WORKLOADS[name]
+    g = h // (w.Hq // w.Hkv)
+    q = W.gen_head(w, "q", b, h)[None, None]
+    k = W.gen_head(w, "k", b, g)[None, None]
+    v = W.gen_head(w, "v", b, g)[None, None]
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=np.asarray(rows))
+    return time.perf_counter() - t0
+
+
+def cpu_share():
+    """Cores this process may use: the affinity mask, capped by a cgroup CPU quota and by
+    OMP_NUM_THREADS when they are set (a shared host's per-job share).  Returns (cores, note)."""
+    aff = len(os.sched_getaffinity(0))
+    cores, why = aff, ["affinity %d" % aff]
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    q = W.gen_head(w, "q", 0, 0)[None, None]
-    k = W.gen_head(w, "k", 0, 0)[None, None]
-    v = W.gen_head(w, "v", 0, 0)[None, None]
-    # calibrate: fixed cost (quantizing K and V of the head) and the per-row cost
-    t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=w.causal, rows=W.sample_rows(w.N, 2))
-    fixed = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=w.causal, rows=W.sample_rows(w.N, 256))
-    per_row = max(time.perf_counter() - t0 - fixed, 1e-3) / 256
-    n = int(min(w.N, max(256, (seconds_target - fixed) / per_row)))
-    rows = W.sample_rows(w.N, n)
-    t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=w.causal, rows=rows)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * rows.size * w.N * w.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
-            "sample": "float64 NumPy oracle forward (quantize K,V of head (0,0), then %d sampled query rows "
-                      "against all %d keys) in %.1f s; metric flops 4*rows*N*d" % (rows.size, w.N, dt),
-            "seconds": dt}
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) / int(per)))
+            why.append("cgroup quota %d" % quota)
+            cores = min(cores, quota)
+    except Exception:
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        why.append("OMP_NUM_THREADS %s" % omp)
+        cores = min(cores, int(omp))
+    return cores, ", ".join(why)
+
+
+def cpu_baseline(w, seconds_target=15.0, chunk=1024):
+    """The oracle, untouched, on a bounded sample of the same workload, spread over the host cores
+    this process may use (one process per core, one BLAS thread each).
+
+    Each task is one call of the oracle forward: one head, ``chunk`` sampled query rows against all
+    keys.  The heads cycle over the tasks; every core keeps one task in flight until about
+    ``seconds_target`` seconds have passed, then the tasks in flight finish.  The full-problem time
+    is extrapolated from the measured rate and labelled as such: the full problem is not run."""
+    import multiprocessing as mp
+    from bit_attention_amd import workloads as W
+    cores, share = cpu_share()
+    H = w.B * w.Hq
+    count = [0]
+
+    def next_task():
+        i = count[0]
+        count[0] += 1
+        hh = i % H
+        rows = W.sample_rows(w.N, chunk, seed=W.BASE_SEED + i).tolist()
+        return (w.name, hh // w.Hq, hh % w.Hq, rows)
+
+    ctx = mp.get_context("spawn")     # fresh interpreters: nothing of this GPU process is inherited
+    saved = {k: os.environ.get(k) for k in _ONE_THREAD_ENV}
+    os.environ.update({k: "1" for k in _ONE_THREAD_ENV})
+    try:
+        pool = ctx.Pool(cores, initializer=_cpu_worker_init)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    with pool:
+        t0 = time.perf_counter()
+        inflight = [pool.apply_async(_cpu_task, (next_task(),)) for _ in range(cores)]
+        done = 0
+        while inflight:
+            inflight[0].wait()
+            still = []
+            for r in inflight:
+                if r.ready():
+                    r.get()
+                    done += 1
+                    if time.perf_counter() - t0 < seconds_target:
+                        still.append(pool.apply_async(_cpu_task, (next_task(),)))
+                else:
+                    still.append(r)
+            inflight = still
+        wall = time.perf_counter() - t0
+    rows = done * chunk
+    flops = 4.0 * rows * w.N * w.d
+    total_rows = w.B * w.Hq * w.N
+    return {"value": flops / wall / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": ("float64 NumPy oracle forward, %d processes (one per core, 1 BLAS thread each; %s); %d "
+                       "calls of %d sampled query rows of one head (heads in turn) against all %d keys; %d rows "
+                       "in %.1f s wall (worker start-up included); metric flops 4*rows*N*d"
+                       % (cores, share, done, chunk, w.N, rows, wall)),
+            "rows_per_s": rows / wall, "seconds": wall,
+            "extrapolated_full_s": total_rows / (rows / wall),
+            "extrapolated_note": ("EXTRAPOLATED, not run: %d query rows of the full problem at the sampled %.1f rows/s"
+                                  % (total_rows, rows / wall))}
+
+
+# ---- accuracy context: cosine similarity against exact fp64 softmax attention ----
+# Plain float64 softmax attention on the unquantized bf16 inputs (textbook formula, no tiling, no
+# quantization); the GPU outputs are compared with it on sampled heads and rows.  Context only:
+# the parity gate is the fake-quant oracle in the tests.
+def _exact_rows(q, k, v, rows, causal):
+    import numpy as np
+    q = q.astype(np.float64)[rows]
+    s = (q @ k.astype(np.float64).T) / np.sqrt(q.shape[-1])
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= np.asarray(rows)[:, None], s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ v.astype(np.float64)
+
+
+def _cosine(a, b):
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def fwd_cosine(w, x, o_dev, heads=None, nrows=256):
+    """Cosine of the GPU forward output with exact fp64 attention over sampled rows of some heads.
+    x: the workload's host inputs (bf16-valued float32 [B, H, N, d]); o_dev: the GPU O."""
+    from bit_attention_amd import workloads as W
+    heads = heads if heads is not None else sorted({(0, 0), (w.B - 1, w.Hq - 1)})
+    rows = W.sample_rows(w.N, nrows)
+    got, ref = [], []
+    for b, h in heads:
+        g = h // (w.Hq // w.Hkv)
+        ref.append(_exact_rows(x["q"][b, h], x["k"][b, g], x["v"][b, g], rows, w.causal))
+        got.append(o_dev[b, h, rows].float().cpu().numpy())
+    return {"cos_O": _cosine(got, ref), "heads": [list(h) for h in heads], "rows_per_head": int(rows.size)}
+
+
+def bwd_cosine(w, x, dq, dk, dv, b=0, h=0):
+    """Cosine of the GPU gradients (one head, all rows and keys) with the exact fp64 gradients of
+    softmax attention at the unquantized inputs (D from the exact output)."""
+    import numpy as np
+    q, k, v, do = (x[t][b, h].astype(np.float64) for t in ("q", "k", "v", "do"))
+    sc = 1.0 / np.sqrt(q.shape[-1])
+    s = (q @ k.T) * sc
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ v
+    dp = do @ v.T
+    ds = p * (dp - np.sum(do * o, axis=1, keepdims=True))
+    del s, dp
+    ref = {"dQ": (ds @ k) * sc, "dK": (ds.T @ q) * sc, "dV": p.T @ do}
+    got = {"dQ": dq[b, h], "dK": dk[b, h], "dV": dv[b, h]}
+    return {"cos_" + n: _cosine(got[n].float().cpu().numpy(), ref[n]) for n in ref}
 
 
 def bench_backward(args, torch, ops, W):
@@ -152,6 +286,10 @@ def bench_backward(args, torch, ops, W):
     except ops.AttnFp4Error as e:
         return {"workload": w.name, "status": str(e)}
     dq, dk, dv = res
+    torch.cuda.synchronize()
+    acc = fwd_cosine(w, x, o)
+    acc.update(bwd_cosine(w, x, dq, dk, dv))
+    del x
     ws = torch.empty(ops.attn_fp4_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8,
                      device="cuda")
     stream = torch.cuda.current_stream()
@@ -165,7 +303,7 @@ def bench_backward(args, torch, ops, W):
     fp4 = 2.0 * w.d * pairs
     bf16 = 8.0 * w.d * pairs
     t_roof = fp4 / (PEAK_FP4_TFLOPS * 1e9) + bf16 / (PEAK_BF16_TFLOPS * 1e9)
-    return {"workload": w.name, "ms": ms, "fp4_flops": fp4, "bf16_flops": bf16,
+    return {"workload": w.name, "ms": ms, "accuracy": acc, "fp4_flops": fp4, "bf16_flops": bf16,
             "tflops_total": (fp4 + bf16) / ms / 1e9, "roofline_ms": t_roof, "frac": t_roof / ms}
 
 
@@ -173,16 +311,18 @@ def bench_forward_configs(args, torch, ops, W):
     """The forward alone on the other forward workloads (causal LLM shape, GQA prefill), seeded
     inputs, HIP events on its stream; flops count the visible (query, key) pairs, 4 d each."""
     out = {}
-    for name in ("llm_causal_b2h16n4096d128", "gqa_causal_b1hq32hkv8n16384d128"):
+    for name in ("tiny_b1h2n256d64", "llm_causal_b2h16n4096d128", "gqa_causal_b1hq32hkv8n16384d128"):
         w = W.WORKLOADS[name]
         x = gen_inputs(w, ["q", "k", "v"])
         dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
-        del x
         qq = ops.attn_fp4_quantize(dev["q"], 0)
         kq = ops.attn_fp4_quantize(dev["k"], 0)
         vq = ops.attn_fp4_quantize(dev["v"], 1)
         del dev
         o, m, l = ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal)
+        torch.cuda.synchronize()
+        acc = fwd_cosine(w, x, o)
+        del x
         fn = lambda: ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal, o=o, m=m, l=l)
         for _ in range(2):
             fn()
@@ -190,7 +330,8 @@ def bench_forward_configs(args, torch, ops, W):
         ms = time_region(fn, max(5, args.steps), torch.cuda.current_stream())
         pairs = w.B * w.Hq * (w.N * (w.N + 1) // 2 if w.causal else w.N * w.N)
         tf = 4.0 * w.d * pairs / ms / 1e9
-        out[name] = {"ms": ms, "visible_pairs": pairs, "tflops": tf, "frac_mfma": tf / PEAK_FP4_TFLOPS}
+        out[name] = {"ms": ms, "visible_pairs": pairs, "tflops": tf, "frac_mfma": tf / PEAK_FP4_TFLOPS,
+                     "accuracy": acc}
     return out
 
 
@@ -281,6 +422,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true", help="only time the CPU oracle (no GPU)")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fwd-only-reps", type=int, default=0,
                     help="if > 0: only run the forward kernel this many times (for profilers)")
@@ -299,6 +441,11 @@ def main():
               "(the single-GPU kernel is what scales; see the sharding notes). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_baseline_only:
+        from bit_attention_amd import workloads as W
+        print(json.dumps(cpu_baseline(W.WORKLOADS["dit_b1h24n32768d128"])), flush=True)
+        return
 
     import torch
     from bit_attention_amd import ops
@@ -330,7 +477,6 @@ def main():
     x = gen_inputs(w, ["q", "k", "v"])
     log("  %.1f s" % (time.perf_counter() - t0))
     dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
-    del x
     B, H, N, d = w.B, w.Hq, w.N, w.d
     qc = torch.empty((B, H, N, d // 2), dtype=torch.uint8, device="cuda")
     qs = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device="cuda")
@@ -370,6 +516,8 @@ def main():
         step()
     torch.cuda.synchronize()
     log("warmup done")
+    acc_main = fwd_cosine(w, x, o)
+    del x
     # timed region: exactly K steps, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -423,10 +571,22 @@ def main():
     log("forward_configs", result["forward_configs"])
     result["kvcache"] = bench_kvcache(args, torch, ops, W)
     log("kvcache", result["kvcache"])
+    # accuracy context: cosine of the GPU outputs with exact fp64 softmax attention
+    accuracy = {w.name: acc_main}
+    for name, r in result["forward_configs"].items():
+        accuracy[name] = r["accuracy"]
+    if "backward" in result and "accuracy" in result["backward"]:
+        accuracy[result["backward"]["workload"]] = result["backward"]["accuracy"]
+    result["accuracy"] = {"reference": "exact float64 softmax attention (and its gradients) on the unquantized "
+                                       "bf16 inputs; sampled rows of the first and last heads (gradients: one "
+                                       "whole head)", "cosine": accuracy}
+    log("accuracy", result["accuracy"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w)
-        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "rows_per_s",
+                                                     "extrapolated_full_s", "extrapolated_note")}
+        log("cpu_baseline", result["cpu_baseline"])
     print(json.dumps(result), flush=True)
 
 

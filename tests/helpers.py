@@ -41,6 +41,26 @@ def compare(gpu, ref, what, bf16_out=True, rel_tol=REL_L2_TOL, abs_tol=MAX_ABS_T
     return info
 
 
+L_REL_TOL = 1e-4
+
+
+def compare_l(gpu, ref, what, rel_tol=L_REL_TOL):
+    """Row sums of P~: element-wise |gpu - ref| <= rel_tol * ref (the GPU sums the same quantized
+    codes in fp32; rows with ref = 0, which see no key, must be exactly 0).  Returns the largest
+    relative error."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), what + ": non-finite l"
+    empty = ref == 0
+    assert np.all(gpu[empty] == 0), what + ": l of a row that sees no key is not 0"
+    r = np.abs(gpu - ref)[~empty] / ref[~empty]
+    worst = float(r.max(initial=0.0))
+    print("%s: largest relative l error %.2e" % (what, worst))
+    assert worst <= rel_tol, "%s: relative l error %.3e > %.1e" % (what, worst, rel_tol)
+    return worst
+
+
 def cosine(a, b):
     a = np.asarray(a, dtype=np.float64).ravel()
     b = np.asarray(b, dtype=np.float64).ravel()

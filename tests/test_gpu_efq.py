@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from bit_attention_amd import workloads as W
-from helpers import compare, cosine, to_dev
+from helpers import compare, compare_l, cosine, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def gpu_fwd_efq(q, k, v, causal):
 def check(o, m, l, ro, rm, rl, label):
     info = compare(o, ro, label + " O")
     assert np.max(np.abs(m - rm)) <= 1e-5 * max(1.0, np.abs(rm).max()), label
-    compare(l, rl, label + " l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())
+    compare_l(l, rl, label + " l")
     return info
 
 

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from bit_attention_amd import workloads as W
-from helpers import compare, cosine, to_dev
+from helpers import compare, compare_l, cosine, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +48,9 @@ def check_rows(w, q, k, v, o, m, l, heads, rows, label):
                                      causal=w.causal, rows=rows)
         info = compare(o[b, h, rows], ro[0, 0], "%s O head (%d,%d)" % (label, b, h))
         assert np.max(np.abs(m[b, h, rows] - rm[0, 0])) <= 1e-5 * max(1.0, np.abs(rm).max()), label
-        # l = sum of P~: a P~ code that flips at a rounding boundary (fp32 here, fp64 in the oracle)
-        # moves l by one E2M1 step of one element, so l gets the rel-L2 bar of the outputs
-        compare(l[b, h, rows], rl[0, 0], label + " l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())
+        # l = the sum of the same P~ codes, accumulated in fp32 with the history rescales; held
+        # element-wise to 1e-4 relative (fp32 accumulation over 512 tiles stays near 2e-5)
+        compare_l(l[b, h, rows], rl[0, 0], label + " l")
         print("%s head (%d,%d): rel-L2 %.3e max-abs %.3e" % (label, b, h, info["rel_l2"], info["max_abs"]))
 
 
@@ -61,7 +61,7 @@ def test_tiny_full_parity_and_cosine():
     ro, rm, rl = oracle.attn_fwd(q, k, v, causal=w.causal)
     info = compare(o, ro, w.name)
     assert np.max(np.abs(m - rm)) < 1e-5
-    compare(l, rl, w.name + " l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())
+    compare_l(l, rl, w.name + " l")
     ex = oracle.softmax_attention(q, k, v)
     print("%s: rel-L2 %.3e max-abs %.3e cosine(GPU, exact attention) %.5f cosine(oracle, exact) %.5f" % (
         w.name, info["rel_l2"], info["max_abs"], cosine(o, ex), cosine(ro, ex)))

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from bit_attention_amd import workloads as W
-from helpers import compare, to_dev
+from helpers import compare, compare_l, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def check(o, m, l, ro, rm, rl, label):
     info = compare(o[full], ro[full], label + " O")
     assert np.max(np.abs(m[full] - rm[full]), initial=0.0) <= 1e-5 * max(1.0, np.abs(rm[full]).max(initial=0.0)), label
     if full.any():
-        compare(l[full], rl[full], label + " l", bf16_out=False, abs_tol=1e-2 * np.abs(rl[full]).max())
+        compare_l(l[full], rl[full], label + " l")
     return info
 
 

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from bit_attention_amd import workloads as W
-from helpers import compare, to_dev
+from helpers import compare, compare_l, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
@@ -115,7 +115,7 @@ def check_fwd(q, k, v, causal, o, m, l, heads, rows, label):
                                      rows=rows, fmt="nv", nv_tensor_scales=scales)
         info = compare(o[b, h, rows], ro[0, 0], "%s O head (%d,%d)" % (label, b, h))
         assert np.max(np.abs(m[b, h, rows] - rm[0, 0])) <= 1e-5 * max(1.0, np.abs(rm).max()), label
-        compare(l[b, h, rows], rl[0, 0], label + " l", bf16_out=False, abs_tol=1e-2 * np.abs(rl).max())
+        compare_l(l[b, h, rows], rl[0, 0], label + " l")
         print("%s head (%d,%d): rel-L2 %.3e max-abs %.3e" % (label, b, h, info["rel_l2"], info["max_abs"]),
               flush=True)
 

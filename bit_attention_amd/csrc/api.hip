@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 6;
+constexpr int32_t kAbiVersion = 7;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -128,7 +128,9 @@ int64_t attn_fp4_fwd_kvcache_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv,
   return attnfp4::kv_split_plan(B, Hq, Hkv, Nq, Nk, d).total;
 }
 
-int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
+// The cache forward with the split workspace given explicitly (workspace == nullptr: one pass).
+static int32_t fwd_kvcache_impl(const attn_fp4_fwd_kvcache_args* a, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
   if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
   int32_t st0 = check_kvcache_dims(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
   if (st0 != ATTN_FP4_OK) return st0;
@@ -140,8 +142,8 @@ int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   if (!(a->softmax_scale <= 0.0f || std::isfinite(a->softmax_scale))) return ATTN_FP4_E_INVALID_ARG;
   if (a->p_rule != ATTN_FP4_P_EXP && a->p_rule != ATTN_FP4_P_EFQ) return ATTN_FP4_E_INVALID_ARG;
   const attnfp4::KvSplit ks = attnfp4::kv_split_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
-  if (a->workspace != nullptr && ks.splits > 1 &&
-      ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0 || a->workspace_bytes < ks.total))
+  if (workspace != nullptr && ks.splits > 1 &&
+      ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < ks.total))
     return ATTN_FP4_E_WORKSPACE;
   int32_t st = check_device();
   if (st != ATTN_FP4_OK) return st;
@@ -165,8 +167,8 @@ int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   p.splits = 1;
   p.tps = a->Nk / 64;
   p.ws_smax = p.ws_m = p.ws_l = p.ws_o = nullptr;
-  if (a->workspace != nullptr && ks.splits > 1) {
-    uint8_t* w = (uint8_t*)a->workspace;
+  if (workspace != nullptr && ks.splits > 1) {
+    uint8_t* w = (uint8_t*)workspace;
     p.splits = ks.splits;
     p.tps = ks.tps;
     p.ws_smax = (float*)(w + ks.smax);
@@ -180,6 +182,45 @@ int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
   hipError_t e = attnfp4::launch_fwd_kvcache(p, (int)a->d, a->causal != 0, a->p_rule == ATTN_FP4_P_EFQ,
                                              (hipStream_t)stream);
   return e == hipSuccess ? ATTN_FP4_OK : ATTN_FP4_E_HIP;
+}
+
+int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  return fwd_kvcache_impl(a, a->workspace, a->workspace_bytes, stream);
+}
+
+// ---- the cache forward for callers that cannot allocate ----
+// Its split workspace is this file-scope device array: one copy on every GPU the library runs on,
+// held until the process ends.  In host code the array's name is only a handle; its device
+// address on the current GPU comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[ATTN_FP4_KVCACHE_SCRATCH_BYTES];
+static void* g_scratch[64];   // per device: the array's device address (null until looked up)
+
+static int32_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_FP4_E_HIP;
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return ATTN_FP4_E_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return ATTN_FP4_OK;
+}
+
+int32_t attn_fp4_fwd_kvcache_noalloc(const attn_fp4_fwd_kvcache_args* a, void* stream) {
+  if (a == nullptr) return ATTN_FP4_E_INVALID_ARG;
+  int32_t st = check_kvcache_dims(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
+  if (st != ATTN_FP4_OK) return st;
+  const attnfp4::KvSplit ks = attnfp4::kv_split_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nk, a->d);
+  if (ks.splits <= 1) return fwd_kvcache_impl(a, nullptr, 0, stream);   // one pass: no workspace
+  if (ks.total > (int64_t)ATTN_FP4_KVCACHE_SCRATCH_BYTES) return ATTN_FP4_E_WORKSPACE;
+  st = check_device();
+  if (st != ATTN_FP4_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != ATTN_FP4_OK) return st;
+  return fwd_kvcache_impl(a, ws, ATTN_FP4_KVCACHE_SCRATCH_BYTES, stream);
 }
 
 int64_t attn_fp4_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d) {

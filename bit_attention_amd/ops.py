@@ -31,6 +31,7 @@ EXPORTED = (
     "attn_fp4_fwd",
     "attn_fp4_fwd_kvcache",
     "attn_fp4_fwd_kvcache_workspace_bytes",
+    "attn_fp4_fwd_kvcache_noalloc",
     "attn_fp4_bwd_workspace_bytes",
     "attn_fp4_bwd_recompute",
     "attn_fp4_nv_quantize",
@@ -126,6 +127,8 @@ def lib():
         L.attn_fp4_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.attn_fp4_fwd_kvcache.restype = ctypes.c_int32
         L.attn_fp4_fwd_kvcache.argtypes = [ctypes.POINTER(FwdKvcacheArgs), ctypes.c_void_p]
+        L.attn_fp4_fwd_kvcache_noalloc.restype = ctypes.c_int32
+        L.attn_fp4_fwd_kvcache_noalloc.argtypes = [ctypes.POINTER(FwdKvcacheArgs), ctypes.c_void_p]
         L.attn_fp4_fwd_kvcache_workspace_bytes.restype = ctypes.c_int64
         L.attn_fp4_fwd_kvcache_workspace_bytes.argtypes = [ctypes.c_int64] * 6
         L.attn_fp4_bwd_workspace_bytes.restype = ctypes.c_int64
@@ -233,18 +236,10 @@ def attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d):
     return int(lib().attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
 
 
-def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k=None,
-                         causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP,
-                         workspace="auto"):
-    """Forward of Nq new query rows against a pre-quantized key/value cache of capacity Nk.
-
-    q_codes [B, Hq, Nq, d/2]; k_codes [B, Hkv, Nk, d/2]; v_codes [B, Hkv, Nk/32, d, 16] (the cache
-    quantized as a whole); seqlens_k: int32 device tensor [B] of valid cache lengths, or None for
-    Nk.  The new rows are the last Nq positions of each sequence (bottom-right causal alignment).
-    workspace: "auto" allocates the split forward's workspace when the shape uses one; None runs
-    the one-pass kernel; a uint8 CUDA tensor is used as given.
-    Returns (o bf16 [B, Hq, Nq, d], m fp32 [B, Hq, Nq], l fp32 [B, Hq, Nq]).
-    """
+def _kvcache_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k, causal, softmax_scale,
+                  o, m, l, p_rule, workspace):
+    """Check the cache forward's operands, allocate missing outputs, fill the argument struct.
+    workspace: "auto", None or a uint8 CUDA tensor (see attn_fp4_fwd_kvcache)."""
     B, Hq, Nq, dh = q_codes.shape
     d = 2 * dh
     Hkv, Nk = k_codes.shape[1], k_codes.shape[2]
@@ -280,7 +275,39 @@ def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales
                        None if workspace is None else _ptr(workspace),
                        0 if workspace is None else workspace.numel(),
                        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(softmax_scale), int(p_rule))
+    return a, o, m, l
+
+
+def attn_fp4_fwd_kvcache(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k=None,
+                         causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None, p_rule=P_EXP,
+                         workspace="auto"):
+    """Forward of Nq new query rows against a pre-quantized key/value cache of capacity Nk.
+
+    q_codes [B, Hq, Nq, d/2]; k_codes [B, Hkv, Nk, d/2]; v_codes [B, Hkv, Nk/32, d, 16] (the cache
+    quantized as a whole); seqlens_k: int32 device tensor [B] of valid cache lengths, or None for
+    Nk.  The new rows are the last Nq positions of each sequence (bottom-right causal alignment).
+    workspace: "auto" allocates the split forward's workspace when the shape uses one; None runs
+    the one-pass kernel; a uint8 CUDA tensor is used as given.
+    Returns (o bf16 [B, Hq, Nq, d], m fp32 [B, Hq, Nq], l fp32 [B, Hq, Nq]).
+    """
+    a, o, m, l = _kvcache_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k, causal,
+                               softmax_scale, o, m, l, p_rule, workspace)
     _check(lib().attn_fp4_fwd_kvcache(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd_kvcache")
+    return o, m, l
+
+
+KVCACHE_SCRATCH_BYTES = 16 * 1024 * 1024   # ATTN_FP4_KVCACHE_SCRATCH_BYTES of include/attn_fp4.h
+
+
+def attn_fp4_fwd_kvcache_noalloc(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k=None,
+                                 causal=False, softmax_scale=0.0, o=None, m=None, l=None, stream=None,
+                                 p_rule=P_EXP):
+    """attn_fp4_fwd_kvcache whose split workspace is the library's own device array (the C call
+    allocates nothing; pass o, m, l to allocate nothing here either).  Calls that overlap on one
+    GPU share that array and race."""
+    a, o, m, l = _kvcache_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, seqlens_k, causal,
+                               softmax_scale, o, m, l, p_rule, None)
+    _check(lib().attn_fp4_fwd_kvcache_noalloc(ctypes.byref(a), _stream(stream)), "attn_fp4_fwd_kvcache_noalloc")
     return o, m, l
 
 

@@ -211,6 +211,26 @@ int64_t attn_fp4_fwd_kvcache_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv,
 int32_t attn_fp4_fwd_kvcache(const attn_fp4_fwd_kvcache_args* args, void* stream);
 
 /*
+ * attn_fp4_fwd_kvcache_noalloc -- attn_fp4_fwd_kvcache for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight decode
+ * loops, harnesses that forbid hipMalloc).  Same arguments, layouts, results
+ * and errors, except that args->workspace and args->workspace_bytes are
+ * ignored: when the split path applies, its workspace is a device array inside
+ * the library of ATTN_FP4_KVCACHE_SCRATCH_BYTES, one copy on every GPU the
+ * library runs on, held until the process ends.  The call allocates and frees
+ * nothing.  The array keeps the last call's contents; nothing in it needs to
+ * start at zero.  All calls on one GPU share that GPU's array, so calls that
+ * overlap on one GPU (concurrent streams, or threads) race: the caller orders
+ * them, e.g. on one stream.  Its device address is looked up on the first
+ * call on each device (with that device current).
+ * Errors: as attn_fp4_fwd_kvcache; ATTN_FP4_E_WORKSPACE when the shape's split
+ * workspace (attn_fp4_fwd_kvcache_workspace_bytes) exceeds
+ * ATTN_FP4_KVCACHE_SCRATCH_BYTES (use attn_fp4_fwd_kvcache with a workspace).
+ */
+#define ATTN_FP4_KVCACHE_SCRATCH_BYTES (16 * 1024 * 1024)
+int32_t attn_fp4_fwd_kvcache_noalloc(const attn_fp4_fwd_kvcache_args* args, void* stream);
+
+/*
  * Backward arguments.  Quantized operands as for the forward; o, m, l are
  * the forward's outputs; do_ is bf16 [B, Hq, N, d].  Outputs dq bf16
  * [B, Hq, N, d], dk and dv bf16 [B, Hkv, N, d] (summed over the query heads

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = ops.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert ops.attn_fp4_abi_version() == 6
+    assert ops.attn_fp4_abi_version() == 7
 
 
 def test_status_strings():

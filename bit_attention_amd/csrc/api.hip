@@ -64,7 +64,10 @@ int32_t attn_fp4_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int32
   if (bh <= 0 || n <= 0 || d <= 0) return ATTN_FP4_E_INVALID_ARG;
   if (axis != 0 && axis != 1) return ATTN_FP4_E_INVALID_ARG;
   if (d % 32 != 0) return ATTN_FP4_E_INVALID_ARG;
-  if (axis == 1 && (n % 32 != 0 || bh > 65535 || (n + 127) / 128 > 0x7FFFFFFF)) return ATTN_FP4_E_INVALID_ARG;
+  // axis 0: one thread per four 8-element groups; axis 1: one thread per (32-token block,
+  // channel pair); each grid must fit 32 bits
+  if (axis == 0 && (bh * n * (d / 8) + 1023) / 1024 > 0x7FFFFFFF) return ATTN_FP4_E_INVALID_ARG;
+  if (axis == 1 && (n % 32 != 0 || (bh * (n / 32) * (d / 2) + 255) / 256 > 0x7FFFFFFF)) return ATTN_FP4_E_INVALID_ARG;
   int32_t st = check_device();
   if (st != ATTN_FP4_OK) return st;
   hipError_t e = attnfp4::launch_quantize(x, bh, n, d, axis, codes, scales, (hipStream_t)stream);

@@ -18,16 +18,29 @@ namespace attnfp4 {
 
 // ---- axis 0 (Q, K): blocks along the contiguous last axis -------------------------------
 // One lane converts 8 consecutive elements (one 16-byte load); the four lanes of a DPP quad
-// form one 32-element block and agree on its scale through two quad permutations.
+// form one 32-element block and agree on its scale through two quad permutations.  A thread
+// takes RQ_PER such groups, 256 groups apart, with all its loads issued before the first
+// conversion; the loads are non-temporal (the input is read once).  Measured on one bench-shape
+// tensor (24 x 32768 x 128): 41 us against 46 us for one group per thread in a grid-stride loop.
+constexpr int RQ_PER = 4;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const uint4* __restrict__ x,
                                                             uint32_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
                                                             int64_t n8) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;   // multiple of 4: quads stay whole
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n8; g += stride) {
-    uint4 w = x[g];
-    float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+  const int64_t base = (int64_t)blockIdx.x * (256 * RQ_PER) + threadIdx.x;
+  v4u w[RQ_PER];
+#pragma unroll
+  for (int p = 0; p < RQ_PER; ++p) {
+    const int64_t g = base + 256 * p;
+    w[p] = g < n8 ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + g)) : v4u{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int p = 0; p < RQ_PER; ++p) {
+    const int64_t g = base + 256 * p;     // quads stay whole: n8 is a multiple of 4
+    if (g >= n8) return;
+    float f[8] = {bf16_lo(w[p][0]), bf16_hi(w[p][0]), bf16_lo(w[p][1]), bf16_hi(w[p][1]),
+                  bf16_lo(w[p][2]), bf16_hi(w[p][2]), bf16_lo(w[p][3]), bf16_hi(w[p][3])};
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(f[i]) & 0x7FFFFFFFu);
@@ -49,34 +62,25 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const uint4* __restr
 // ---- axis 1 (V): blocks along the sequence, written block-major --------------------------
 // Output layout [n/32][d][16 code bytes] and [n/32][d] scales: the codes of one 32-token block
 // for every channel, then the next block, so that a 64-key tile of V^ is one contiguous run.
-// Grid (ceil(n / 128), ceil(d / 128), bh); 256 threads per 128-token x 128-channel tile.  The tile
-// is read with coalesced 16-byte loads into LDS ([token][channel pair], 272-byte rows), then each
-// thread takes one channel pair and one 32-token block: two complete MX blocks, whose 16 code
-// bytes per channel land next to those of the neighbouring channels.
-constexpr int QC_TOK = 128, QC_CH = 128, QC_PITCH = 68;   // dwords per LDS row (64 + 4 padding)
+// One thread per (32-token block, channel pair): it reads the pair's 32 tokens straight from
+// global memory (consecutive threads hold consecutive channel pairs, so each of the 32 loads of
+// a wave is one contiguous 256-byte row segment), converts its two MX blocks and writes their
+// 2 x 16 code bytes and two scale bytes next to those of the neighbouring pairs.  No LDS and no
+// barrier: every wave keeps its 32 (non-temporal) loads in flight.  Measured on one bench-shape
+// tensor: 40 us, against 45-56 us for the earlier LDS-staged form.
 __global__ void __launch_bounds__(256) quantize_cols_kernel(const uint32_t* __restrict__ x,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            int64_t n, int64_t d) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[QC_TOK * QC_PITCH];
-  const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.z;
-  const int64_t t0 = (int64_t)blockIdx.x * QC_TOK, c0 = (int64_t)blockIdx.y * QC_CH;
-  const int ntok = (int)min((int64_t)QC_TOK, n - t0);       // multiple of 32
-  const int nch = (int)min((int64_t)QC_CH, d - c0);         // multiple of 32
-  const uint32_t* xs = x + (bh * n + t0) * (d / 2) + c0 / 2;
-  for (int k = tid; k < QC_TOK * 16; k += 256) {
-    const int r = k >> 4, cc = k & 15;                      // token, 8-channel chunk
-    if (r < ntok && 8 * cc < nch)
-      *reinterpret_cast<uint4*>(&tile[r * QC_PITCH + 4 * cc]) =
-          *reinterpret_cast<const uint4*>(xs + (int64_t)r * (d / 2) + 4 * cc);
-  }
-  __syncthreads();
-  const int cp = tid & 63, tb = tid >> 6;                   // channel pair, 32-token block
-  if (2 * cp >= nch || 32 * tb >= ntok) return;
+                                                            int64_t n, int64_t d, int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t dp = d / 2, nb = n / 32;
+  const int64_t cp = idx % dp, rest = idx / dp;   // channel pair; (head, block)
+  const int64_t blk = rest % nb, bh = rest / nb;
+  const uint32_t* xs = x + (bh * n + blk * 32) * dp + cp;
   uint32_t w[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i] = tile[(32 * tb + i) * QC_PITCH + cp];
+  for (int i = 0; i < 32; ++i) w[i] = __builtin_nontemporal_load(xs + (int64_t)i * dp);
   uint32_t a0 = 0, a1 = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -101,8 +105,7 @@ __global__ void __launch_bounds__(256) quantize_cols_kernel(const uint32_t* __re
     c0w[q] = u;
     c1w[q] = t;
   }
-  const int64_t ch0 = c0 + 2 * cp;
-  const int64_t blk = (t0 >> 5) + tb;               // 32-token block
+  const int64_t ch0 = 2 * cp;
   uint8_t* cb = codes + bh * d * (n / 2) + (blk * d + ch0) * 16;
   *reinterpret_cast<uint4*>(cb) = make_uint4(c0w[0], c0w[1], c0w[2], c0w[3]);
   *reinterpret_cast<uint4*>(cb + 16) = make_uint4(c1w[0], c1w[1], c1w[2], c1w[3]);
@@ -113,14 +116,13 @@ hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int 
                            void* scales, hipStream_t stream) {
   if (axis == 0) {
     const int64_t n8 = bh * n * d / 8;
-    int64_t blocks = (n8 + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    const int64_t blocks = (n8 + 256 * RQ_PER - 1) / (256 * RQ_PER);
     hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint4*)x, (uint32_t*)codes, (uint8_t*)scales, n8);
   } else {
-    dim3 grid((unsigned)((n + QC_TOK - 1) / QC_TOK), (unsigned)((d + QC_CH - 1) / QC_CH), (unsigned)bh);
-    hipLaunchKernelGGL(quantize_cols_kernel, grid, dim3(256), 0, stream, (const uint32_t*)x,
-                       (uint8_t*)codes, (uint8_t*)scales, n, d);
+    const int64_t total = bh * (n / 32) * (d / 2);   // (block, channel pair) items
+    hipLaunchKernelGGL(quantize_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       (const uint32_t*)x, (uint8_t*)codes, (uint8_t*)scales, n, d, total);
   }
   return hipGetLastError();
 }

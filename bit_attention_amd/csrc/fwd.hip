@@ -66,6 +66,20 @@ struct Stage {
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
 
+// Largest of w[0 .. n): sixteen independent loads per round trip (indices past the end repeat the
+// last element, which leaves the maximum unchanged), rather than one dependent load per element.
+__device__ __forceinline__ float prefix_max(const float* __restrict__ w, int n) {
+  float m = -__builtin_inff();
+  for (int s0 = 0; s0 < n; s0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = w[min(s0 + u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m = fmaxf(m, v[u]);
+  }
+  return m;
+}
+
 // Key held by LDS slot s (0..63) of a tile.  Slots 32T..32T+31 are the A rows of S^T MFMA T; in the
 // 32x32 output layout, register r of lane l holds row 8(r/4) + 4(l/32) + r%4, and this map makes
 // that row key 32(l/32) + 16T + r: lane l then holds all 32 keys of P block l/32 for query l%32.
@@ -288,8 +302,7 @@ fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();
   const int64_t RKs = SPLIT ? p.Nq * G : 0;       // packed rows per KV head (workspace rows)
   if constexpr (SPLIT) {                          // the running max carried into this range
-    if (valid)
-      for (int64_t s2 = 0; s2 < sp; ++s2) m_run = fmaxf(m_run, p.ws_smax[(bh * RKs + prow) * nsp + s2]);
+    if (valid) m_run = prefix_max(p.ws_smax + (bh * RKs + prow) * nsp, (int)sp);
   }
   const float c = p.c;
 
@@ -495,9 +508,11 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t G = p.Hq / p.Hkv, RK = p.Nq * G, nqt = (RK + 63) / 64, nsp = p.splits;
-  int64_t id = blockIdx.x;
-  const int64_t sp = id % nsp;
-  id /= nsp;
+  // consecutive workgroups take the same range of different row groups, so that the early ranges
+  // (which every sequence has) and the late ones (which only long sequences have) spread evenly
+  const int64_t ngrp = nqt * p.Hkv * p.B;
+  const int64_t sp = blockIdx.x / ngrp;
+  const int64_t id = blockIdx.x - sp * ngrp;
   const int64_t bh = id / nqt, qt = id - bh * nqt;
   const int64_t b = bh / p.Hkv, g = bh - b * p.Hkv;
   const int64_t pr0 = qt * 64;
@@ -546,10 +561,11 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
                                                     kc_rs, key * (D / 2) + 32 * ks + 16 * hi, tt * (64 * D / 2), 0));
       }
     };
-    Ops cur, nxt;
-    load(t0, cur);
-    for (int t = t0; t < te; t += tstep) {
-      if (t + tstep < te) load(t + tstep, nxt);
+    // tile t from cur while the wave's next tile is loaded into nxt: two buffers, the loop
+    // unrolled by two (no buffer copies), the load unconditional (the last tile loads itself once
+    // more), so that no wait before a use of cur has to cover the load just issued
+    auto tile_max = [&](int t, const Ops& cur, Ops& nxt) __attribute__((always_inline)) {
+      load(min(t + tstep, te - 1), nxt);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         v16f acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(cur.ka[T][0]), widen(qb[0]), v16f{}, 4, 4, 0,
@@ -566,7 +582,13 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
       }
-      cur = nxt;
+    };
+    Ops ba, bb;
+    load(t0, ba);
+    for (int t = t0; t < te; t += 2 * tstep) {
+      tile_max(t, ba, bb);
+      if (t + tstep >= te) break;
+      tile_max(t + tstep, bb, ba);
     }
   }
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -606,8 +628,7 @@ __global__ void __launch_bounds__(256) kv_merge_kernel(FwdParams p) {
   const float* wm = p.ws_m + rid * nsp;
   const float* wl = p.ws_l + rid * nsp;
   const float* wo = p.ws_o + rid * nsp * D + CPL * lane;
-  float M = -__builtin_inff();
-  for (int s = 0; s < nr; ++s) M = fmaxf(M, wm[s]);
+  const float M = prefix_max(wm, nr);
   float acc[CPL] = {};
   float lt = 0.0f;
   if (M != -__builtin_inff()) {

@@ -8,10 +8,12 @@ HBM before the timed region.  The metric counts 4*B*H*N^2*d flops per step.
 Printed: one JSON line with the step throughput, a roofline object for the dominant kernel (the
 fused forward, timed alone with HIP events on the stream it runs on), the backward of the QAT
 workload (B=1, H=16, N=8192, d=128) measured the same way, the forward with the exp-free EFQ
-probability codes, the forward over NVFP4-style operands (E4M3 scale per 16 elements, bf16
-matrix core, fp16 operands) on the same inputs, the forward on the causal LLM and GQA-prefill workloads, the
-cache forward on a decode batch and a chunked-prefill step, and the CPU oracle timed on a bounded
-sample of the same workload.
+probability codes, the forward over NVFP4-style operands (E4M3 scale per 16 elements, fp16
+operands on the fp16 matrix core) on the same inputs, the forward on the causal LLM and
+GQA-prefill workloads, the cache forward on a decode batch and a chunked-prefill step, and the CPU
+oracle timed on a bounded sample of the same workload.  The secondary workloads are timed once the
+GPU runs at its steady clock (settle_and_time); the step itself takes exactly --warmup untimed
+steps, then --steps timed ones.
 """
 
 import argparse

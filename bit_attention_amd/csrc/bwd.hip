@@ -65,12 +65,22 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
   const int per = d / 16;                       // 8 (d = 128) or 4 (d = 64) elements per lane
   const uint16_t* orow = o + r * d + sub * per;
   const uint16_t* grow = dout + r * d + sub * per;
+  // the lane's O and dO elements in one load each (16 bytes at d = 128, 8 at d = 64)
+  uint32_t ow[4] = {0, 0, 0, 0}, gw[4] = {0, 0, 0, 0};
+  if (per == 8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(orow), g = *reinterpret_cast<const uint4*>(grow);
+    ow[0] = a.x; ow[1] = a.y; ow[2] = a.z; ow[3] = a.w;
+    gw[0] = g.x; gw[1] = g.y; gw[2] = g.z; gw[3] = g.w;
+  } else {
+    const uint2 a = *reinterpret_cast<const uint2*>(orow), g = *reinterpret_cast<const uint2*>(grow);
+    ow[0] = a.x; ow[1] = a.y;
+    gw[0] = g.x; gw[1] = g.y;
+  }
   float acc = 0.0f;
-  for (int i = 0; i < per; i += 2) {
-    const uint32_t a = *reinterpret_cast<const uint32_t*>(orow + i);
-    const uint32_t g = *reinterpret_cast<const uint32_t*>(grow + i);
-    acc = __builtin_fmaf(bf16_lo(a), bf16_lo(g), acc);
-    acc = __builtin_fmaf(bf16_hi(a), bf16_hi(g), acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                 // the zero padding at d = 64 adds nothing
+    acc = __builtin_fmaf(bf16_lo(ow[i]), bf16_lo(gw[i]), acc);
+    acc = __builtin_fmaf(bf16_hi(ow[i]), bf16_hi(gw[i]), acc);
   }
   acc += __shfl_xor(acc, 1, 16);
   acc += __shfl_xor(acc, 2, 16);
@@ -79,8 +89,7 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(const uint16_t* __restric
   const float il = 1.0f / l[r];
   if (sub == 0) *reinterpret_cast<float4*>(rowc + 4 * r) = make_float4(m[r] * kLog2e, il, acc, acc * il);
   if (dos != nullptr) {                         // dO / l, rounded to bf16 once (d = 128)
-    const uint4 gv = *reinterpret_cast<const uint4*>(grow);
-    const uint32_t w[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t* w = gw;
     uint4 out;
     out.x = pk_bf16(bf16_lo(w[0]) * il, bf16_hi(w[0]) * il);
     out.y = pk_bf16(bf16_lo(w[1]) * il, bf16_hi(w[1]) * il);

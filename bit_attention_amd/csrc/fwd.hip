@@ -48,6 +48,7 @@ namespace attnfp4 {
 namespace {
 
 constexpr int BC = 64;  // key-tile width; part of the definition of P quantization
+constexpr int64_t kCuPerXcd = 32;   // MI355X: 256 compute units in 8 XCDs
 
 template <int D>
 struct Stage {
@@ -143,9 +144,23 @@ fwd_kernel(FwdParams p) {
     const int64_t nbh = total / nqt;
     if ((total & 7) == 0 && (nbh & 7) == 0) {
       const int64_t hp = nbh >> 3;                // heads per XCD
-      const int64_t x = id / (total >> 3), j = id - x * (total >> 3);
-      bh = x * hp + j % hp;
-      qt = nqt - 1 - j / hp;
+      const int64_t M = total >> 3;               // work items per XCD
+      const int64_t x = id / M, j = id - x * M;
+      // rank r: longest first.  With three to four workgroups per CU (M in [3R, 4R], R = CUs per
+      // XCD), a CU's first three workgroups are most of its work, and longest-first would start
+      // some CUs with three long ones: there the first three dispatch rounds (one workgroup per CU
+      // each) take the longest R, the shortest R, then the next R longest in ascending order, and
+      // the rest follow longest first.  Measured on the causal LLM shape (M = 4R): 71.6 against
+      // 73.3 us.
+      constexpr int64_t R = kCuPerXcd;
+      int64_t r = j;
+      if (M >= 3 * R && M <= 4 * R) {
+        if (j >= R && j < 2 * R) r = M - R + (j - R);
+        else if (j >= 2 * R && j < 3 * R) r = 2 * R - 1 - (j - 2 * R);
+        else if (j >= 3 * R) r = j - R;
+      }
+      bh = x * hp + r % hp;
+      qt = nqt - 1 - r / hp;
     } else {
       qt = nqt - 1 - qt;
     }

@@ -514,7 +514,8 @@ fwd_kernel(FwdParams p) {
 // does (when the workgroup has at most 32 rows, both waves take them and alternate tiles).  K^ is
 // read straight into the MFMA A operand, one tile ahead (no LDS; keys in natural order: the
 // maximum does not depend on where a key sits), and the scores are the forward's, bit for bit
-// (same operands, scales and k-step order).
+// (same operands, scales and k-step order).  A row group's last range is not run: no range after
+// it reads its maximum.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   constexpr int KS_STEPS = D / 64;
@@ -545,6 +546,9 @@ __global__ void __launch_bounds__(128) kv_max_kernel(FwdParams p) {
   const int lim_wg = lim_of(min(pr0 + 63, RK - 1));
   const int ntl_all = lim_wg >= 0 ? lim_wg / 64 + 1 : 0;
   const int tb = (int)(sp * p.tps);
+  // the group's last range (and any range past it) is skipped: the split forward of range s reads
+  // only the maxima of ranges 0 .. s - 1 (workgroup-uniform)
+  if (ntl_all <= tb + (int)p.tps) return;
   const int te = min(tb + (int)p.tps, min(ntl_all, lim_hi >= 0 ? lim_hi / 64 + 1 : 0));
   const int tstep = share ? 2 : 1;
   float mx = -__builtin_inff();

@@ -306,7 +306,7 @@ fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < KS_STEPS; ++ks)
     kr_off[ks] = S::KC + l32 * (D / 2) + 16 * ((hi + 2 * ks) ^ swz_small(l32, S::KCHUNKS));
-  const int ksr_off = S::KS + 4 * l32;             // + 128 T; the lane's blocks start at byte hi
+  const int ksr_off = S::KS + 4 * l32 + hi;        // + 128 T: the lane's first block (hi) of slot l32
   const int vr_off = S::VC + l32 * 32 + 16 * (hi ^ swz_small(l32 >> 1, 2));
   const int vsr_off = S::VS + D * hi + l32;        // + 32 ct: block hi of channel 32 ct + l32
 
@@ -327,14 +327,15 @@ fwd_kernel(FwdParams p) {
     v16f sT[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      // bytes 0 and 2 after the shift: blocks hi (k-step 0) and 2 + hi (k-step 1) of the slot
-      const int ksc = (int)(*reinterpret_cast<const uint32_t*>(base + ksr_off + 128 * T) >> (8 * hi));
+      // the slot's blocks hi (k-step 0) and 2 + hi (k-step 1), one byte read each
+      const int ksc0 = base[ksr_off + 128 * T];
       const v4i ka0 = *reinterpret_cast<const v4i*>(base + kr_off[0] + T * 32 * (D / 2));
-      sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc, 0, qsc);
+      sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka0), widen(qb[0]), v16f{}, 4, 4, 0, ksc0, 0, qsc);
       if (KS_STEPS == 2) {
+        const int ksc1 = base[ksr_off + 128 * T + 2];
         const v4i ka1 = *reinterpret_cast<const v4i*>(base + kr_off[KS_STEPS - 1] + T * 32 * (D / 2));
-        sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka1), widen(qb[KS_STEPS - 1]), sT[T], 4, 4, 2,
-                                                               ksc, 2, qsc);
+        sT[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(ka1), widen(qb[KS_STEPS - 1]), sT[T], 4, 4, 0,
+                                                               ksc1, 2, qsc);
       }
     }
     if ((CAUSAL || KV) && t * BC + BC - 1 > lim_lo) {   // keys past a row's limit -> -inf
@@ -363,7 +364,7 @@ fwd_kernel(FwdParams p) {
     // E8M0 scale of the block from its max p = exp2((bm - m) c): the biased exponent of p is
     // floor((bm - m) c) + 127 (the row's own maximum gives exactly 0, i.e. p = 1); scale byte =
     // that - 2, clamped below at 1 (affects only P < 2^-124; a fully masked block gives -inf).
-    const int psc = (int)fmaxf(__builtin_floorf((bm - m_sh) * c), -124.0f) + 125;
+    const int psc = (int)__builtin_floorf(fmaxf((bm - m_sh) * c, -124.0f)) + 125;
     const float sc = __uint_as_float((uint32_t)psc << 23);
     // p = exp2(s c - m c) and E2M1 conversion against the block scale; the packed codes are
     // already the B operand of the PV MFMA (lane l: keys 32(l/32) .. +31 of query l%32)

@@ -34,14 +34,16 @@ QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 
 # Measured HBM traffic of one forward launch at the bench shape: rocprofv3 --pmc FETCH_SIZE and
 # --pmc WRITE_SIZE, each scaled by the factor the same counter shows on a plain 1 GiB device copy
-# (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source it was measured on.
+# (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source and build flags it was
+# measured with.
 FWD_TRAFFIC = {"source_sha1": "716cfb3098988e4529d0b1e6446355dc7f4d25de", "bytes": 1.0405e9}
 
 
 def fwd_source_sha1():
     import hashlib
     h = hashlib.sha1()
-    for f in ("bit_attention_amd/csrc/fwd.hip", "bit_attention_amd/csrc/common.h"):
+    for f in ("bit_attention_amd/csrc/fwd.hip", "bit_attention_amd/csrc/fwd_kernel.h", "bit_attention_amd/csrc/common.h",
+              "bit_attention_amd/build.py"):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

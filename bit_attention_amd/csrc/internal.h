@@ -107,6 +107,8 @@ hipError_t launch_quantize(const void* x, int64_t bh, int64_t n, int64_t d, int 
                            void* scales, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
 hipError_t launch_fwd_kvcache(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
+// the split form (p.splits > 1): max pass, split forward, merge
+hipError_t launch_fwd_kvcache_split(const FwdParams& p, int d, bool causal, bool efq, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace attnfp4

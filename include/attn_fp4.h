@@ -29,8 +29,9 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
  *    tensors on ROCm), contiguous, row-major, 16-byte aligned.  The caller
- *    owns and allocates every buffer; the library never allocates, frees,
- *    synchronises or keeps state beyond a cached per-device arch check.
+ *    owns and allocates every buffer; the library never allocates, frees or
+ *    synchronises, and keeps no state beyond two per-device caches: the arch
+ *    check and the device address of the no-alloc entry point's array.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously on it; nothing is waited for.
  *  - Every function returns an attn_fp4_status; argument errors are

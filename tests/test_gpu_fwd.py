@@ -87,7 +87,8 @@ def test_full_size_workloads_sampled_rows(name):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N,d,Hq,Hkv", [(64, 128, 1, 1), (192, 128, 4, 2), (128, 64, 3, 1), (320, 64, 2, 2)])
+@pytest.mark.parametrize("N,d,Hq,Hkv", [(64, 128, 1, 1), (192, 128, 4, 2), (128, 64, 3, 1), (320, 64, 2, 2),
+                                        (256, 128, 8, 1), (192, 64, 8, 2)])
 def test_small_shapes_full(N, d, Hq, Hkv, causal):
     rng = np.random.default_rng(N + d + Hq + int(causal))
     q = W.round_to_bf16(rng.standard_normal((2, Hq, N, d)) * 1.5)

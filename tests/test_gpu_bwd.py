@@ -119,3 +119,18 @@ def test_causal_gqa_mid_size_sampled():
     for name, g, r in (("dQ", dq[:, :, rows], rq), ("dK", dk[:, :, keys], rk), ("dV", dv[:, :, keys], rv)):
         info = compare(g, r, "causal gqa N2048 " + name)
         print("causal gqa N2048 %s rel-L2 %.3e max-abs %.3e" % (name, info["rel_l2"], info["max_abs"]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_deterministic(causal):
+    """No atomics and fixed summation orders: two backward calls give identical bits."""
+    rng = np.random.default_rng(41 + int(causal))
+    N, d, Hq, Hkv = 256, 128, 4, 2
+    q = W.round_to_bf16(rng.standard_normal((1, Hq, N, d)) * 1.5)
+    k = W.round_to_bf16(rng.standard_normal((1, Hkv, N, d)))
+    v = W.round_to_bf16(rng.standard_normal((1, Hkv, N, d)))
+    do = W.round_to_bf16(rng.standard_normal((1, Hq, N, d)) * 0.1)
+    first = run_gpu(q, k, v, do, causal)
+    second = run_gpu(q, k, v, do, causal)
+    for name, a, b in zip(("o", "m", "l", "dq", "dk", "dv"), first, second):
+        assert np.array_equal(a, b, equal_nan=True), name

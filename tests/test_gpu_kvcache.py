@@ -197,3 +197,18 @@ def test_split_workspace_reuse_and_smaller_call():
         torch.cuda.synchronize()
         ro, rm, rl = oracle.attn_fwd_kvcache(q, kc, vc, seqlens, causal=True)
         check(o.float().cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), ro, rm, rl, "reuse Nq=%d" % Nq)
+
+
+def test_split_bitwise_deterministic():
+    """The split path merges its ranges in a fixed order: two calls give identical bits."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 1, 4096, 128
+    seqlens = [4096, 2500]
+    q = rand_bf16((B, Hq, Nq, d), 7500, 1.3)
+    kc = rand_bf16((B, Hkv, Nk, d), 7501)
+    vc = rand_bf16((B, Hkv, Nk, d), 7502)
+    from bit_attention_amd import ops
+    assert ops.attn_fp4_fwd_kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) > 0, "the split path must run"
+    first = gpu_kv(q, kc, vc, seqlens, True)
+    second = gpu_kv(q, kc, vc, seqlens, True)
+    for name, a, b in zip(("o", "m", "l"), first, second):
+        assert np.array_equal(a, b), name

@@ -11,8 +11,9 @@
 //   O = acc / l (bf16), saved m (natural-log units) and l.
 //
 // gfx950 mapping.  One wave owns 32 query rows; a workgroup of W waves shares each 64-key
-// K^/V^ tile through LDS (four stages filled by direct global-to-LDS loads three tiles ahead;
-// one barrier per tile).  On gfx950 the matrix core and the vector ALU barely overlap, so a tile
+// K^/V^ tile through LDS (stages filled by direct global-to-LDS loads: three tiles computed per
+// barrier from one half of six stages while the other half is refilled, see tiles_per_step).  On
+// gfx950 the matrix core and the vector ALU barely overlap, so a tile
 // costs about the sum of its MFMA time and its VALU time (exp, E2M1 conversion, max, FMA); the
 // kernel is shaped for three waves per SIMD, which measured best, and keeps everything else (tile
 // loads, LDS reads, barriers) under that sum.
@@ -99,6 +100,20 @@ __device__ __forceinline__ int slot_key(int s) {
 template <int D, int W, bool SPLIT>
 constexpr int waves_per_simd() { return D == 128 ? (W == 4 || SPLIT ? 3 : 2) : 4; }
 
+// Key tiles per barrier.  The plain and one-pass cache forward compute GT tiles from one half of
+// 2 GT LDS stages while the other half is refilled with the next GT tiles, with one barrier per GT
+// tiles: three when 2 x 3 stages for every workgroup the CU holds fit its 160 KB of LDS, else two.
+// Measured against one barrier per tile (four stages, three tiles ahead), outputs identical: video
+// shape 4.82-4.83 against 4.88-4.91 ms, causal GQA 0.858-0.860 against 0.880-0.883 ms, causal LLM
+// 71.5-71.9 against 74.3-74.4 us; two tiles per barrier gained about half as much.  The split
+// forward keeps one tile per barrier over three stages, which lets six of its workgroups share a CU.
+template <int D, int W, bool SPLIT>
+constexpr int tiles_per_step() {
+  if (SPLIT) return 1;
+  constexpr int wg_per_cu = 4 * waves_per_simd<D, W, SPLIT>() / W;
+  return wg_per_cu * 6 * Stage<D>::BYTES <= 160 * 1024 ? 3 : 2;
+}
+
 // KV selects the cache forward: Nq new query rows per head against a cache of capacity Nk per KV
 // head holding L_b valid keys for sequence b.  New row i sits at position L_b - Nq + i (causal
 // masking is bottom-right aligned), and the query heads that share a KV head are packed into the
@@ -119,9 +134,10 @@ fwd_kernel(FwdParams p) {
   constexpr int NT = 64 * W;                      // threads
   constexpr int KS_STEPS = D / 64;                // MFMA k-steps over the head dim
   constexpr int CT = D / 32;                      // 32-channel output tiles
-  constexpr int NSTAGE = SPLIT ? 3 : 4;            // LDS stages; tiles are loaded NSTAGE - 1 ahead
+  constexpr int GT = tiles_per_step<D, W, SPLIT>();
+  constexpr int NSTAGE = SPLIT ? 3 : 2 * GT;       // LDS stages
   constexpr int PD = NSTAGE - 1;
-  static_assert(NSTAGE >= 3 && NSTAGE <= 4, "stages");
+  static_assert(NSTAGE >= 3 && NSTAGE <= 6, "stages");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
 
@@ -446,36 +462,55 @@ fwd_kernel(FwdParams p) {
   if (SPLIT && ntiles <= 0) return;                                      // whole workgroup
   const int last_active = lim_hi >= 0 ? lim_hi / BC : -1;                // wave-uniform
 
-  // The barrier that ends step t publishes tile t + 1: each wave first waits for its own DMAs up
-  // to that tile's (all but the JPW issued by each later step), and for its LDS reads (the stage
-  // of tile t is refilled in step t + 1).  The asm statements also keep the compiler from moving
-  // memory accesses across the barrier.
-  for (int k = 0; k < PD; ++k)
-    if (k < ntiles) issue_tile(tb + k, smem + k * S::BYTES);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  static_assert(2 * JPW <= 15, "vmcnt immediate");
-  auto step = [&](int t, auto stc) {
-    constexpr int st = decltype(stc)::value;
-    if (t + PD < ntiles) issue_tile(tb + t + PD, smem + ((st + PD) % NSTAGE) * S::BYTES);
-    if (tb + t <= last_active) tile(tb + t, smem + st * S::BYTES);
-    const int newer = min(max(ntiles - t - 2, 0), PD - 1);   // later steps that issued DMAs
-    if (PD > 2 && newer >= 2)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * JPW) : "memory");
-    else if (newer >= 1)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(JPW) : "memory");
-    else
+  // Every barrier publishes staged tiles and frees stages: each wave first waits for its own DMAs
+  // (s_waitcnt vmcnt) and its LDS reads (lgkmcnt), so that after the barrier every wave may read
+  // the tiles just landed and refill the stages just read.  The asm statements also keep the
+  // compiler from moving memory accesses across the barrier.
+  if constexpr (!SPLIT) {
+    // GT tiles per step: the step computing from one half of the stages first refills the other
+    // half, freed by the barrier that ended the previous step, with the next GT tiles
+    for (int k = 0; k < GT; ++k)
+      if (k < ntiles) issue_tile(tb + k, smem + k * S::BYTES);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto group = [&](int t, auto hc) {
+      constexpr int s0 = decltype(hc)::value ? GT : 0, l0 = GT - s0;
+#pragma unroll
+      for (int i = 0; i < GT; ++i)
+        if (t + GT + i < ntiles) issue_tile(tb + t + GT + i, smem + (l0 + i) * S::BYTES);
+#pragma unroll
+      for (int i = 0; i < GT; ++i)
+        if (t + i < ntiles && tb + t + i <= last_active) tile(tb + t + i, smem + (s0 + i) * S::BYTES);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  for (int t = 0; t < ntiles; t += NSTAGE) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 >= ntiles) break;
-    step(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 >= ntiles) break;
-    step(t + 2, std::integral_constant<int, 2>{});
-    if constexpr (NSTAGE > 3) {
-      if (t + 3 >= ntiles) break;
-      step(t + 3, std::integral_constant<int, 3>{});
+    };
+    for (int t = 0; t < ntiles; t += 2 * GT) {
+      group(t, std::integral_constant<int, 0>{});
+      if (t + GT >= ntiles) break;
+      group(t + GT, std::integral_constant<int, 1>{});
+    }
+  } else {
+    // one tile per step over three stages, two tiles ahead: the barrier that ends step t publishes
+    // tile t + 1 (all DMAs but the JPW that step t issued for tile t + 2 have landed) and frees the
+    // stage of tile t, which step t + 1 refills
+    static_assert(NSTAGE == 3, "stages");
+    for (int k = 0; k < PD; ++k)
+      if (k < ntiles) issue_tile(tb + k, smem + k * S::BYTES);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(JPW <= 15, "vmcnt immediate");
+    auto step = [&](int t, auto stc) {
+      constexpr int st = decltype(stc)::value;
+      if (t + PD < ntiles) issue_tile(tb + t + PD, smem + ((st + PD) % NSTAGE) * S::BYTES);
+      if (tb + t <= last_active) tile(tb + t, smem + st * S::BYTES);
+      if (t + PD < ntiles)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(JPW) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    for (int t = 0; t < ntiles; t += NSTAGE) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 >= ntiles) break;
+      step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 >= ntiles) break;
+      step(t + 2, std::integral_constant<int, 2>{});
     }
   }
 

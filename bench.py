@@ -36,7 +36,7 @@ QUANT_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 # --pmc WRITE_SIZE, each scaled by the factor the same counter shows on a plain 1 GiB device copy
 # (FETCH_SIZE 2.000, WRITE_SIZE 1.000).  Valid only for the kernel source and build flags it was
 # measured with.
-FWD_TRAFFIC = {"source_sha1": "aec2f66966e41e89719e69e2cb0acfe8ad20bdf1", "bytes": 1.0566e9}
+FWD_TRAFFIC = {"source_sha1": "cb67b95ae4d3517fc52d1ad2da2e2090a320eb86", "bytes": 1.0566e9}
 
 
 def fwd_source_sha1():

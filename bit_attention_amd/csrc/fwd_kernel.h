@@ -138,6 +138,8 @@ fwd_kernel(FwdParams p) {
   constexpr int NSTAGE = SPLIT ? 3 : 2 * GT;       // LDS stages
   constexpr int PD = NSTAGE - 1;
   static_assert(NSTAGE >= 3 && NSTAGE <= 6, "stages");
+  static_assert(4 * waves_per_simd<D, W, SPLIT>() / W * NSTAGE * Stage<D>::BYTES <= 160 * 1024,
+                "the stages of every workgroup the intended occupancy puts on a CU fit its LDS");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * S::BYTES];
 

@@ -163,7 +163,7 @@ def _cpu_task(a):
     k = W.gen_head(w, "k", b, g)[None, None]
     v = W.gen_head(w, "v", b, g)[None, None]
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal=w.causal, rows=np.asarray(rows))
+    oracle.attn_fwd(q, k, v, causal=w.causal, rows=None if rows is None else np.asarray(rows))
     return time.perf_counter() - t0
 
 
@@ -187,9 +187,11 @@ def cpu_share():
     return cores, ", ".join(why)
 
 
-def cpu_baseline(w, seconds_target=15.0, chunk=1024):
+def cpu_baseline(w, seconds_target=15.0, chunk=1024,
+                 full_workloads=("tiny_b1h2n256d64", "llm_causal_b2h16n4096d128")):
     """The oracle, untouched, on a bounded sample of the same workload, spread over the host cores
-    this process may use (one process per core, one BLAS thread each).
+    this process may use (one process per core, one BLAS thread each).  Before it, the small
+    workloads in ``full_workloads`` are run in full over the same pool (a few seconds).
 
     Each task is one call of the oracle forward: one head, ``chunk`` sampled query rows against all
     keys.  The heads cycle over the tasks; every core keeps one task in flight until about
@@ -220,6 +222,19 @@ def cpu_baseline(w, seconds_target=15.0, chunk=1024):
             else:
                 os.environ[k] = v
     with pool:
+        # the two small workloads in full first (every row of every head; one task per head)
+        full = {}
+        for name in full_workloads:
+            fw = W.WORKLOADS[name]
+            tasks = [(name, b, h, None) for b in range(fw.B) for h in range(fw.Hq)]
+            t0 = time.perf_counter()
+            for r in [pool.apply_async(_cpu_task, (t,)) for t in tasks]:
+                r.get()
+            fwall = time.perf_counter() - t0
+            pairs = fw.B * fw.Hq * (fw.N * (fw.N + 1) // 2 if fw.causal else fw.N * fw.N)
+            full[name] = {"wall_s": fwall, "rows": fw.B * fw.Hq * fw.N, "heads": len(tasks),
+                          "tflops": 4.0 * pairs * fw.d / fwall / 1e12,
+                          "note": "full problem run (not sampled); visible pairs for causal"}
         t0 = time.perf_counter()
         inflight = [pool.apply_async(_cpu_task, (next_task(),)) for _ in range(cores)]
         done = 0
@@ -244,7 +259,7 @@ def cpu_baseline(w, seconds_target=15.0, chunk=1024):
                        "calls of %d sampled query rows of one head (heads in turn) against all %d keys; %d rows "
                        "in %.1f s wall (worker start-up included); metric flops 4*rows*N*d"
                        % (cores, share, done, chunk, w.N, rows, wall)),
-            "rows_per_s": rows / wall, "seconds": wall,
+            "rows_per_s": rows / wall, "seconds": wall, "full_runs": full,
             "extrapolated_full_s": total_rows / (rows / wall),
             "extrapolated_note": ("EXTRAPOLATED, not run: %d query rows of the full problem at the sampled %.1f rows/s"
                                   % (total_rows, rows / wall))}
@@ -611,7 +626,7 @@ def main():
         log("timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(w)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "rows_per_s",
-                                                     "extrapolated_full_s", "extrapolated_note")}
+                                                     "extrapolated_full_s", "extrapolated_note", "full_runs")}
         log("cpu_baseline", result["cpu_baseline"])
     print(json.dumps(result), flush=True)
 

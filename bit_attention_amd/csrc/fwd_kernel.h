@@ -155,9 +155,18 @@ fwd_kernel(FwdParams p) {
   const int64_t nsp = SPLIT ? p.splits : 1;
   const int64_t total = nqt * (KV ? p.Hkv : p.Hq) * p.B * nsp;
   int64_t id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int64_t sp = SPLIT ? id % nsp : 0;        // key-tile range (split forward)
-  id = SPLIT ? id / nsp : id;
+  int64_t sp = 0;                                 // key-tile range (split forward)
+  if constexpr (SPLIT) {
+    // range-major, as in kv_max_kernel: workgroup i runs on XCD i % 8, so each XCD takes the
+    // same share of every sequence's ranges.  A sequence per XCD (the remap below) left the XCD
+    // holding the longest cache with the most bytes to stream (1.4x the mean for lengths drawn
+    // from U[N/4, N] over eight sequences).
+    const int64_t ngrp = total / nsp;
+    sp = id / ngrp;
+    id -= sp * ngrp;
+  } else if ((total & 7) == 0) {
+    id = (id & 7) * (total >> 3) + (id >> 3);
+  }
   int64_t bh = id / nqt;                          // (b, query head), cache forward: (b, KV head)
   int64_t qt = id - bh * nqt;
   if (CAUSAL && !SPLIT) {

@@ -464,6 +464,9 @@ def main():
                     help="if > 0: only run the QAT-workload backward this many times (for profilers)")
     ap.add_argument("--kv-only-reps", type=int, default=0,
                     help="if > 0: only run the decode cache forward this many times (for profilers)")
+    ap.add_argument("--causal-only-reps", type=int, default=0,
+                    help="if > 0: only run the causal LLM and causal GQA forwards this many times each "
+                         "(for profilers)")
     ap.add_argument("--nv-only-reps", type=int, default=0,
                     help="if > 0: only run the NVFP4-style forward this many times (for profilers)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -496,11 +499,26 @@ def main():
         return
 
     global _QUICK
-    _QUICK = args.bwd_only_reps > 0 or args.kv_only_reps > 0 or args.nv_only_reps > 0
+    _QUICK = args.bwd_only_reps > 0 or args.kv_only_reps > 0 or args.nv_only_reps > 0 or args.causal_only_reps > 0
 
     if args.bwd_only_reps > 0:
         args.steps = args.bwd_only_reps
         log("backward", bench_backward(args, torch, ops, W))
+        return
+
+    if args.causal_only_reps > 0:
+        for name in ("llm_causal_b2h16n4096d128", "gqa_causal_b1hq32hkv8n16384d128"):
+            w = W.WORKLOADS[name]
+            x = gen_inputs(w, ["q", "k", "v"])
+            dev = {t: torch.from_numpy(a).to(torch.bfloat16).cuda() for t, a in x.items()}
+            qq = ops.attn_fp4_quantize(dev["q"], 0)
+            kq = ops.attn_fp4_quantize(dev["k"], 0)
+            vq = ops.attn_fp4_quantize(dev["v"], 1)
+            o, m, l = ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal)
+            for _ in range(args.causal_only_reps):
+                ops.attn_fp4_fwd(*qq, *kq, *vq, causal=w.causal, o=o, m=m, l=l)
+            torch.cuda.synchronize()
+            log("%s: %d forwards" % (name, args.causal_only_reps))
         return
 
     if args.kv_only_reps > 0:

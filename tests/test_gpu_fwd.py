@@ -99,6 +99,48 @@ def test_small_shapes_full(N, d, Hq, Hkv, causal):
     compare(o, ro, "N%d d%d Hq%d Hkv%d causal%d" % (N, d, Hq, Hkv, causal))
 
 
+def _tile_max_rises(q, k, causal, bc=64):
+    """Fraction of (row, visible key tile after the first) at which the running max of the
+    quantized scores rises (CPU, from the oracle's quantizer)."""
+    qh = oracle.fake_quant_mx(q.astype(np.float64), axis=-1)[0, 0]
+    kh = oracle.fake_quant_mx(k.astype(np.float64), axis=-1)[0, 0]
+    s = qh @ kh.T
+    N = s.shape[0]
+    if causal:
+        s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+    tmax = s.reshape(N, N // bc, bc).max(axis=2)
+    run = np.maximum.accumulate(tmax, axis=1)
+    rises = run[:, 1:] > run[:, :-1]
+    visible = np.arange(1, N // bc)[None, :] * bc <= np.arange(N)[:, None] if causal else np.ones_like(rises)
+    return float(rises[visible].mean())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_history_rescale_on_every_tile_or_none(order, causal):
+    """Scores that rise along the keys make nearly every key tile raise every row's running max, so
+    the history rescale runs on each tile with alpha < 1; scores that fall leave the max where the
+    first tile put it, so the rescale never runs after it.  Both against the oracle; the per-tile
+    maxima are checked on the CPU first, so that the inputs do what they are meant to."""
+    rng = np.random.default_rng(23 + int(causal) + 2 * (order == "rising"))
+    N, d, H = 2048, 128, 2
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    t = np.linspace(0.5, 12.0, N) if order == "rising" else np.linspace(12.0, 0.5, N)
+    k = W.round_to_bf16(t[None, None, :, None] * u * np.sqrt(d) + 0.05 * rng.standard_normal((1, H, N, d)))
+    q = W.round_to_bf16((1.0 + 0.2 * rng.random((1, H, N, 1))) * u + 0.05 * rng.standard_normal((1, H, N, d)))
+    v = W.round_to_bf16(rng.standard_normal((1, H, N, d)))
+    frac = _tile_max_rises(q[:, :1], k[:, :1], causal)
+    print("%s causal=%d: running max rises at %.3f of the visible tiles" % (order, causal, frac))
+    assert (frac > 0.95) if order == "rising" else (frac < 0.02)
+    o, m, l = gpu_fwd(q, k, v, causal)
+    ro, rm, rl = oracle.attn_fwd(q, k, v, causal=causal)
+    info = compare(o, ro, "%s causal=%d" % (order, causal))
+    assert np.max(np.abs(m - rm)) <= 1e-5 * max(1.0, np.abs(rm).max())
+    compare_l(l, rl, "%s causal=%d l" % (order, causal))
+    print("%s causal=%d: rel-L2 %.3e max-abs %.3e" % (order, causal, info["rel_l2"], info["max_abs"]))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_q_gives_mean_of_quantized_v(causal):
     """Closed form: Q = 0 -> every P~ = 1, O_i = mean of V^ rows (causal: prefix mean), l_i = count."""

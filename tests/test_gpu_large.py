@@ -1,7 +1,8 @@
 """Parity at the largest sizes this suite runs: a 131072-token head through the forward (MXFP4 and
-NVFP4-style), a 131072-key decode through the split cache forward, and a 2^27-element
-quantization (both formats), each launched whole and compared with the oracle on sampled rows,
-heads or blocks (rows, heads and blocks are independent, so each sample is exact parity)."""
+NVFP4-style), a 32768-token GQA group through the backward, a 131072-key decode through the split
+cache forward, and a 2^27-element quantization (both formats), each launched whole and compared
+with the oracle on sampled rows, heads or blocks (rows, heads and blocks are independent, so each
+sample is exact parity)."""
 
 import numpy as np
 import pytest
@@ -37,6 +38,29 @@ def test_forward_131072_tokens_sampled_rows(causal):
     compare(o, ro[0, 0], "N=131072 O")
     assert np.max(np.abs(m - rm[0, 0])) <= 1e-5 * max(1.0, np.abs(rm).max())
     compare_l(l, rl[0, 0], "N=131072 l")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_32768_tokens_gqa_sampled(causal):
+    """The backward over two query heads sharing one KV head at N = 32768 (512 key tiles per query
+    row, 256 key blocks per head): dQ on sampled query rows, dK and dV (summed over the two query
+    heads) on sampled 32-key blocks, against the oracle fed the GPU forward's O and l."""
+    from test_gpu_bwd import run_gpu
+    N, d = 32768, 128
+    q = rand_bf16((1, 2, N, d), 8300 + causal, 1.2)
+    k = rand_bf16((1, 1, N, d), 8302)
+    v = rand_bf16((1, 1, N, d), 8303)
+    do = rand_bf16((1, 2, N, d), 8304, 0.1)
+    o, m, l, dq, dk, dv = run_gpu(q, k, v, do, causal)
+    rows = np.array([0, 1, 63, 64, 4095, 16384, 29999, N - 65, N - 2, N - 1])
+    blocks = np.array([0, 1, 255, 256, 511, 700, N // 32 - 2, N // 32 - 1])
+    keys = (blocks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    m_ref = oracle.attn_row_max(q, k, causal=causal)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, o, do, m_ref, l, causal=causal, rows=rows, key_blocks=blocks)
+    for name, g, r in (("dQ", dq[:, :, rows], rq), ("dK", dk[:, :, keys], rk), ("dV", dv[:, :, keys], rv)):
+        info = compare(g, r, "N=32768 backward causal=%d %s" % (causal, name))
+        print("N=32768 backward causal=%d %s rel-L2 %.3e max-abs %.3e" % (causal, name, info["rel_l2"],
+                                                                          info["max_abs"]))
 
 
 def test_decode_131072_keys_split():
